@@ -1,0 +1,191 @@
+"""MI355X (gfx950) FlashAttention: a thin Python binding over libfa.so.
+
+The functions named like the C entry points (``fa_fwd``, ``fa_fwd_blocked``,
+``fa_bwd``, ``fa_bwd_workspace_size``, ``fa_decode_split``,
+``fa_merge_states``, ``fa_status_str``) only check and marshal torch tensors
+into the C ABI of ``include/fa.h``; every step of the computation runs in the
+library's HIP kernels.  ``forward``, ``backward`` and ``decode`` additionally
+allocate the outputs with torch before calling them.
+
+torch provides device memory and streams only.  It is imported before
+libfa.so is loaded so that both use the one HIP runtime already in the
+process.  There is no fallback: if libfa.so is missing, importing this module
+raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_F32, FA_BF16 = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                      "(hipcc --offload-arch=gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_vp, _i64, _f32, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+_lib.fa_fwd.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _int,
+                        _vp]
+_lib.fa_fwd_blocked.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                _f32, _int, _i64, _vp]
+_lib.fa_bwd_workspace_size.argtypes = [_int, _i64, _i64, _i64, _i64]
+_lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
+_lib.fa_bwd.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                        _i64, _i64, _i64, _i64, _i64, _f32, _int, _vp]
+_lib.fa_decode_split.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                 _i64, _i64, _f32, _vp]
+_lib.fa_merge_states.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                 _vp]
+_lib.fa_status_str.argtypes = [_int]
+_lib.fa_status_str.restype = ctypes.c_char_p
+for _f in ("fa_fwd", "fa_fwd_blocked", "fa_bwd", "fa_decode_split", "fa_merge_states"):
+    getattr(_lib, _f).restype = _int
+
+EXPORTS = ("fa_fwd", "fa_fwd_blocked", "fa_bwd_workspace_size", "fa_bwd", "fa_decode_split",
+           "fa_merge_states", "fa_status_str")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_str(status)}")
+
+
+def fa_status_str(status: int) -> str:
+    return _lib.fa_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != FA_OK:
+        raise FaError(status, where)
+
+
+_DT = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _scale(d: int, scale) -> float:
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def _bhnd(t: torch.Tensor):
+    if t.dim() != 4:
+        raise ValueError("expected a [B, H, N, d] tensor")
+    return t.shape
+
+
+def fa_fwd(q, k, v, o, lse, scale=None, causal=False, stream=None) -> None:
+    B, H, Nq, d = _bhnd(q)
+    Nk = _bhnd(k)[2]
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    _check(_lib.fa_fwd(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                       _scale(d, scale), int(bool(causal)), _stream(stream)), "fa_fwd")
+
+
+def fa_fwd_blocked(q, k, v, o, lse, kv_block, scale=None, causal=False, stream=None) -> None:
+    B, H, Nq, d = _bhnd(q)
+    Nk = _bhnd(k)[2]
+    _check(_lib.fa_fwd_blocked(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq,
+                               Nk, d, _scale(d, scale), int(bool(causal)), int(kv_block),
+                               _stream(stream)), "fa_fwd_blocked")
+
+
+def fa_bwd_workspace_size(dtype, B, H, Nq, d) -> int:
+    dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(_lib.fa_bwd_workspace_size(dt, B, H, Nq, d))
+
+
+def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, workspace, scale=None, causal=False,
+           stream=None) -> None:
+    B, H, Nq, d = _bhnd(q)
+    Nk = _bhnd(k)[2]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.fa_bwd(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                       _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, Nq, Nk, d,
+                       _scale(d, scale), int(bool(causal)), _stream(stream)), "fa_bwd")
+
+
+def fa_decode_split(q, k, v, part_m, part_l, part_o, n_split, scale=None, stream=None) -> None:
+    B, H, Nq, d = _bhnd(q)
+    Nk = _bhnd(k)[2]
+    _check(_lib.fa_decode_split(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(part_m), _ptr(part_l),
+                                _ptr(part_o), B, H, Nq, Nk, d, int(n_split), _scale(d, scale),
+                                _stream(stream)), "fa_decode_split")
+
+
+def fa_merge_states(part_m, part_l, part_o, o, lse, stream=None) -> None:
+    B, H, Nq, n_split = part_m.shape
+    d = o.shape[-1]
+    _check(_lib.fa_merge_states(_dt(o), _ptr(part_m), _ptr(part_l), _ptr(part_o), _ptr(o),
+                                _ptr(lse), B, H, Nq, d, n_split, _stream(stream)),
+           "fa_merge_states")
+
+
+# ---------------------------------------------------------------------------
+# Convenience wrappers that allocate outputs with torch.
+# ---------------------------------------------------------------------------
+def forward(q, k, v, scale=None, causal=False, kv_block=None, stream=None):
+    """(O, L) for Q [B,H,Nq,d], K, V [B,H,Nk,d]; L is fp32 [B,H,Nq]."""
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    if kv_block is None:
+        fa_fwd(q, k, v, o, lse, scale, causal, stream)
+    else:
+        fa_fwd_blocked(q, k, v, o, lse, kv_block, scale, causal, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, lse, do, scale=None, causal=False, stream=None):
+    """(dQ, dK, dV) of <O, dO>; O and L from forward() with the same arguments."""
+    B, H, Nq, d = q.shape
+    ws = torch.empty(fa_bwd_workspace_size(q.dtype, B, H, Nq, d), dtype=torch.uint8,
+                     device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, scale, causal, stream)
+    return dq, dk, dv
+
+
+def decode(q, k, v, n_split, scale=None, stream=None, out_dtype=None):
+    """Split-KV decoding: returns (O, L, (part_m, part_l, part_o))."""
+    B, H, Nq, d = q.shape
+    dev = q.device
+    pm = torch.empty((B, H, Nq, n_split), dtype=torch.float32, device=dev)
+    pl = torch.empty_like(pm)
+    po = torch.empty((B, H, Nq, n_split, d), dtype=torch.float32, device=dev)
+    fa_decode_split(q, k, v, pm, pl, po, n_split, scale, stream)
+    o = torch.empty((B, H, Nq, d), dtype=out_dtype or q.dtype, device=dev)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    fa_merge_states(pm, pl, po, o, lse, stream)
+    return o, lse, (pm, pl, po)

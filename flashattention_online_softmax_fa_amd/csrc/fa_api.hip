@@ -1,0 +1,151 @@
+// fa_api.hip -- the C ABI (include/fa.h): argument checks, then one launcher
+// per call.  Nothing is enqueued unless every check passes.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return p != nullptr && ((uintptr_t)p % a) == 0; }
+
+// All sizes >= 1 and every element count used below fits comfortably in int64.
+bool sizes_ok(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return false;
+    int64_t bh, x;
+    if (__builtin_mul_overflow(B, H, &bh)) return false;
+    const int64_t n = Nq > Nk ? Nq : Nk;
+    if (__builtin_mul_overflow(bh, n, &x)) return false;
+    if (__builtin_mul_overflow(x, d, &x)) return false;
+    return x < (int64_t(1) << 60);
+}
+
+size_t elem_size(fa_dtype dt) { return dt == FA_BF16 ? 2 : 4; }
+
+bool dtype_ok(fa_dtype dt) { return dt == FA_F32 || dt == FA_BF16; }
+
+constexpr int64_t kMaxGrid = 2147483647;
+
+fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+fa_status fwd_common(fa_dtype dt, const void *Q, const void *K, const void *V, void *O, float *L,
+                     int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                     int causal, int64_t kv_block, void *stream) {
+    if (!dtype_ok(dt)) return FA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H, Nq, Nk, d)) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    const uintptr_t al = dt == FA_BF16 ? 16 : 4;
+    if (!aligned(Q, al) || !aligned(K, al) || !aligned(V, al) || !aligned(O, al) ||
+        !aligned(L, 4))
+        return FA_ERR_INVALID_ARG;
+    fa::FwdArgs a{Q, K, V, O, L, B, H, Nq, Nk, d, scale, causal, kv_block};
+    if (dt == FA_F32) {
+        if (d > 128) return FA_ERR_UNSUPPORTED;
+        if ((B * H * Nq + 3) / 4 > kMaxGrid) return FA_ERR_UNSUPPORTED;
+        return hip_status(fa::launch_fwd_f32(a, (hipStream_t)stream));
+    }
+    if (kv_block != 0) return FA_ERR_UNSUPPORTED;  // the bf16 path has fixed tiles
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (B * H * ((Nq + 63) / 64) > kMaxGrid) return FA_ERR_UNSUPPORTED;
+    return hip_status(fa::launch_fwd_bf16(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(fa_dtype dt, const void *Q, const void *K, const void *V, void *O, float *L,
+                 int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                 int causal, void *stream) {
+    return fwd_common(dt, Q, K, V, O, L, B, H, Nq, Nk, d, scale, causal, 0, stream);
+}
+
+fa_status fa_fwd_blocked(fa_dtype dt, const void *Q, const void *K, const void *V, void *O,
+                         float *L, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                         float scale, int causal, int64_t kv_block, void *stream) {
+    if (dt != FA_F32) return dt == FA_BF16 ? FA_ERR_UNSUPPORTED : FA_ERR_INVALID_ARG;
+    if (kv_block < 1 || kv_block > 256) return FA_ERR_INVALID_ARG;
+    return fwd_common(dt, Q, K, V, O, L, B, H, Nq, Nk, d, scale, causal, kv_block, stream);
+}
+
+size_t fa_bwd_workspace_size(fa_dtype dt, int64_t B, int64_t H, int64_t Nq, int64_t d) {
+    if (!dtype_ok(dt) || !sizes_ok(B, H, Nq, 1, d)) return 0;
+    const size_t rows = (size_t)(B * H * Nq);
+    const size_t d_bytes = (rows * 4 + 255) / 256 * 256;
+    const size_t acc_bytes = (rows * (size_t)d * 4 + 255) / 256 * 256;
+    return d_bytes + acc_bytes;
+}
+
+fa_status fa_bwd(fa_dtype dt, const void *Q, const void *K, const void *V, const void *O,
+                 const float *L, const void *dO, void *dQ, void *dK, void *dV, void *workspace,
+                 size_t ws_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                 float scale, int causal, void *stream) {
+    if (!dtype_ok(dt)) return FA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H, Nq, Nk, d)) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    const uintptr_t al = dt == FA_BF16 ? 16 : 4;
+    if (!aligned(Q, al) || !aligned(K, al) || !aligned(V, al) || !aligned(O, al) ||
+        !aligned(dO, al) || !aligned(dQ, al) || !aligned(dK, al) || !aligned(dV, al) ||
+        !aligned(L, 4) || !aligned(workspace, 256))
+        return FA_ERR_INVALID_ARG;
+    const size_t need = fa_bwd_workspace_size(dt, B, H, Nq, d);
+    if (ws_bytes < need) return FA_ERR_INVALID_ARG;
+    if (dt != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (B * H * ((Nk + 63) / 64) > kMaxGrid || B * H * ((Nq + 63) / 64) > kMaxGrid)
+        return FA_ERR_UNSUPPORTED;
+    const size_t rows = (size_t)(B * H * Nq);
+    float *D = (float *)workspace;
+    float *acc = (float *)((char *)workspace + (rows * 4 + 255) / 256 * 256);
+    fa::BwdArgs a{Q, K, V, O, dO, L, dQ, dK, dV, D, acc, B, H, Nq, Nk, d, scale, causal};
+    return hip_status(fa::launch_bwd_bf16(a, (hipStream_t)stream));
+}
+
+fa_status fa_decode_split(fa_dtype dt, const void *Q, const void *K, const void *V,
+                          float *part_m, float *part_l, float *part_o, int64_t B, int64_t H,
+                          int64_t Nq, int64_t Nk, int64_t d, int64_t n_split, float scale,
+                          void *stream) {
+    if (!dtype_ok(dt)) return FA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H, Nq, Nk, d)) return FA_ERR_INVALID_ARG;
+    if (n_split < 1 || n_split > (int64_t(1) << 20)) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+    const uintptr_t al = dt == FA_BF16 ? 16 : 4;
+    if (!aligned(Q, al) || !aligned(K, al) || !aligned(V, al) || !aligned(part_m, 4) ||
+        !aligned(part_l, 4) || !aligned(part_o, 4))
+        return FA_ERR_INVALID_ARG;
+    if (dt != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (B * H * Nq > kMaxGrid / n_split) return FA_ERR_UNSUPPORTED;
+    fa::DecodeArgs a{Q, K, V, part_m, part_l, part_o, B, H, Nq, Nk, d, n_split, scale};
+    return hip_status(fa::launch_decode_split_bf16(a, (hipStream_t)stream));
+}
+
+fa_status fa_merge_states(fa_dtype dt, const float *part_m, const float *part_l,
+                          const float *part_o, void *O, float *L, int64_t B, int64_t H,
+                          int64_t Nq, int64_t d, int64_t n_split, void *stream) {
+    if (!dtype_ok(dt)) return FA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H, Nq, 1, d)) return FA_ERR_INVALID_ARG;
+    if (n_split < 1 || n_split > (int64_t(1) << 20)) return FA_ERR_INVALID_ARG;
+    if (!aligned(part_m, 4) || !aligned(part_l, 4) || !aligned(part_o, 4) ||
+        !aligned(O, elem_size(dt)) || !aligned(L, 4))
+        return FA_ERR_INVALID_ARG;
+    if (d > 512) return FA_ERR_UNSUPPORTED;
+    if (B * H * Nq > kMaxGrid) return FA_ERR_UNSUPPORTED;
+    fa::MergeArgs a{part_m, part_l, part_o, O, L, B * H * Nq, d, n_split, dt == FA_BF16};
+    return hip_status(fa::launch_merge_states(a, (hipStream_t)stream));
+}
+
+const char *fa_status_str(fa_status s) {
+    switch (s) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+        case FA_ERR_HIP: return "FA_ERR_HIP";
+    }
+    return "FA_ERR_UNKNOWN";
+}
+
+}  // extern "C"

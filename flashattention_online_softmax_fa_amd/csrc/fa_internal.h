@@ -1,0 +1,53 @@
+// fa_internal.h -- launch interface between the C ABI layer (fa_api.hip) and
+// the kernel files.  Host-side only; the arguments have been validated by the
+// caller, so launchers only pick an instance and a grid.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+    const void *Q, *K, *V;
+    void *O;
+    float *L;
+    int64_t B, H, Nq, Nk, d;
+    float scale;
+    int causal;
+    int64_t kv_block;  // fp32 path: keys per online-softmax step
+};
+
+struct BwdArgs {
+    const void *Q, *K, *V, *O, *dO;
+    const float *L;
+    void *dQ, *dK, *dV;
+    float *D;      // workspace [B][H][Nq]
+    float *dQacc;  // workspace [B][H][Nq][d]
+    int64_t B, H, Nq, Nk, d;
+    float scale;
+    int causal;
+};
+
+struct DecodeArgs {
+    const void *Q, *K, *V;
+    float *part_m, *part_l, *part_o;
+    int64_t B, H, Nq, Nk, d, n_split;
+    float scale;
+};
+
+struct MergeArgs {
+    const float *part_m, *part_l, *part_o;
+    void *O;
+    float *L;
+    int64_t rows, d, n_split;
+    int out_bf16;
+};
+
+hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t s);
+hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s);
+hipError_t launch_decode_split_bf16(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_merge_states(const MergeArgs &a, hipStream_t s);
+
+}  // namespace fa

@@ -1,0 +1,156 @@
+"""The C ABI on the host, without a GPU: the library loads, exports every
+function include/fa.h declares, and rejects bad arguments before it touches
+the HIP runtime (argument checks come first and launch nothing)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+SO = os.path.join(ROOT, "flashattention_online_softmax_fa_amd", "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_F32, FA_BF16 = 0, 1
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(SO):
+        pytest.fail("libfa.so is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(SO)
+    vp, i64, f32, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    lib.fa_fwd.argtypes = [i, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i, vp]
+    lib.fa_fwd_blocked.argtypes = [i, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i, i64,
+                                   vp]
+    lib.fa_bwd_workspace_size.argtypes = [i, i64, i64, i64, i64]
+    lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64,
+                           i64, i64, i64, f32, i, vp]
+    lib.fa_decode_split.argtypes = [i, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32,
+                                    vp]
+    lib.fa_merge_states.argtypes = [i, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp]
+    lib.fa_status_str.argtypes = [i]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    return lib
+
+
+def test_header_declares_the_calls():
+    assert _declared() == sorted(["fa_fwd", "fa_fwd_blocked", "fa_bwd_workspace_size", "fa_bwd",
+                                  "fa_decode_split", "fa_merge_states", "fa_status_str"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_binding_exposes_the_same_names():
+    import flashattention_online_softmax_fa_amd as fa
+    for name in _declared():
+        assert callable(getattr(fa, name)), name
+    assert sorted(fa.EXPORTS) == _declared()
+
+
+def test_status_strings(lib):
+    assert lib.fa_status_str(0) == b"FA_OK"
+    assert lib.fa_status_str(1) == b"FA_ERR_INVALID_ARG"
+    assert lib.fa_status_str(2) == b"FA_ERR_UNSUPPORTED"
+    assert lib.fa_status_str(3) == b"FA_ERR_HIP"
+
+
+# Fake, well-aligned addresses: every call below must be rejected before any
+# pointer is used or any HIP call is made.
+P = 0x10000000
+NULL = None
+
+
+def fwd(lib, **kw):
+    a = dict(dt=FA_BF16, Q=P, K=P, V=P, O=P, L=P, B=1, H=1, Nq=8, Nk=8, d=64, scale=0.125,
+             causal=0)
+    a.update(kw)
+    return lib.fa_fwd(a["dt"], a["Q"], a["K"], a["V"], a["O"], a["L"], a["B"], a["H"], a["Nq"],
+                      a["Nk"], a["d"], a["scale"], a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(Q=NULL), FA_ERR_INVALID_ARG),
+    (dict(L=NULL), FA_ERR_INVALID_ARG),
+    (dict(B=0), FA_ERR_INVALID_ARG),
+    (dict(H=-1), FA_ERR_INVALID_ARG),
+    (dict(Nq=0), FA_ERR_INVALID_ARG),
+    (dict(Nk=0), FA_ERR_INVALID_ARG),
+    (dict(d=0), FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), FA_ERR_INVALID_ARG),
+    (dict(causal=2), FA_ERR_INVALID_ARG),
+    (dict(dt=7), FA_ERR_INVALID_ARG),
+    (dict(Q=P + 8), FA_ERR_INVALID_ARG),          # bf16 needs 16-byte alignment
+    (dict(L=P + 2), FA_ERR_INVALID_ARG),
+    (dict(d=96), FA_ERR_UNSUPPORTED),             # bf16 tiles exist for d = 64, 128
+    (dict(dt=FA_F32, d=129), FA_ERR_UNSUPPORTED),
+    (dict(B=1 << 40, H=1 << 30), FA_ERR_INVALID_ARG),  # element count overflow
+])
+def test_fwd_rejects(lib, kw, want):
+    assert fwd(lib, **kw) == want
+
+
+def test_fwd_blocked_rejects(lib):
+    args = (P, P, P, P, P, 1, 1, 8, 8, 16, 0.25, 0)
+    assert lib.fa_fwd_blocked(FA_F32, *args, 0, None) == FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_blocked(FA_F32, *args, 257, None) == FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_blocked(FA_BF16, *args, 4, None) == FA_ERR_UNSUPPORTED
+
+
+def test_bwd_workspace_size(lib):
+    # D: 2*3*100 floats -> 2400 B -> 2560 (256-aligned); acc: 2*3*100*64*4 = 153600
+    assert lib.fa_bwd_workspace_size(FA_BF16, 2, 3, 100, 64) == 2560 + 153600
+    assert lib.fa_bwd_workspace_size(FA_BF16, 0, 3, 100, 64) == 0
+
+
+def bwd(lib, **kw):
+    need = lib.fa_bwd_workspace_size(FA_BF16, 1, 1, 8, 64)
+    a = dict(dt=FA_BF16, ws=P, ws_bytes=need, d=64, Nq=8, scale=0.125, causal=1, dO=P)
+    a.update(kw)
+    return lib.fa_bwd(a["dt"], P, P, P, P, P, a["dO"], P, P, P, a["ws"], a["ws_bytes"], 1, 1,
+                      a["Nq"], 8, a["d"], a["scale"], a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(ws=NULL), FA_ERR_INVALID_ARG),
+    (dict(ws=P + 16), FA_ERR_INVALID_ARG),        # workspace must be 256-aligned
+    (dict(ws_bytes=100), FA_ERR_INVALID_ARG),
+    (dict(dO=NULL), FA_ERR_INVALID_ARG),
+    (dict(scale=float("-inf")), FA_ERR_INVALID_ARG),
+    (dict(d=32), FA_ERR_UNSUPPORTED),
+    (dict(dt=FA_F32), FA_ERR_UNSUPPORTED),
+])
+def test_bwd_rejects(lib, kw, want):
+    assert bwd(lib, **kw) == want
+
+
+def test_decode_rejects(lib):
+    def call(n_split=4, d=128, dt=FA_BF16, Q=P, pm=P):
+        return lib.fa_decode_split(dt, Q, P, P, pm, P, P, 1, 1, 1, 64, d, n_split, 0.1, None)
+    assert call(n_split=0) == FA_ERR_INVALID_ARG     # at least one split
+    assert call(n_split=-3) == FA_ERR_INVALID_ARG
+    assert call(Q=NULL) == FA_ERR_INVALID_ARG
+    assert call(pm=P + 1) == FA_ERR_INVALID_ARG
+    assert call(d=80) == FA_ERR_UNSUPPORTED
+    assert call(dt=FA_F32) == FA_ERR_UNSUPPORTED
+
+
+def test_merge_rejects(lib):
+    def call(n_split=4, d=128, O=P):
+        return lib.fa_merge_states(FA_BF16, P, P, P, O, P, 1, 1, 1, d, n_split, None)
+    assert call(n_split=0) == FA_ERR_INVALID_ARG
+    assert call(O=NULL) == FA_ERR_INVALID_ARG
+    assert call(O=P + 1) == FA_ERR_INVALID_ARG
+    assert call(d=513) == FA_ERR_UNSUPPORTED

@@ -1,0 +1,123 @@
+"""bf16 matrix-core forward against the oracle.
+
+Tolerances: O max-abs 2e-2 and L max-abs 1e-3 (bf16 inputs are exact in the
+oracle; the GPU rounds P to bf16 before the PV product and O on output).
+Mid sizes are compared on every element and span several 128-query and
+64-key tiles with ragged tails; the full workloads (4 x 16 heads x 2048, d=64;
+32 heads x 8192 causal, d=128, with one K row per head scaled by 30) are
+compared on sampled rows, in the launch configuration the benchmark times."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fa_inputs import make_inputs, workload_inputs
+from tests.gpu_helpers import host, max_abs, say
+
+pytestmark = pytest.mark.gpu
+O_TOL, L_TOL = 2e-2, 1e-3
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import flashattention_online_softmax_fa_amd as m
+    return m
+
+
+def _run(fa, x, scale, causal):
+    o, lse = fa.forward(x.q, x.k, x.v, scale, causal)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [
+    (1, 2, 200, 200, 64),
+    (2, 2, 333, 333, 128),
+    (1, 3, 129, 129, 128),
+    (1, 1, 64, 64, 64),
+    (1, 1, 1, 1, 64),
+    (2, 1, 130, 77, 64),     # Nq != Nk
+    (1, 2, 50, 300, 128),    # Nq < Nk
+])
+def test_full_compare(fa, shape, causal):
+    B, H, Nq, Nk, d = shape
+    x = make_inputs(B, H, Nq, Nk, d, "bf16", seed=sum(shape) + causal, device="cuda")
+    scale = 1 / math.sqrt(d)
+    say(f"bf16 fwd {shape} causal={causal}")
+    o, lse = _run(fa, x, scale, causal)
+    O_ref, L_ref = oracle.dense_fwd(host(x.q), host(x.k), host(x.v), scale, causal)
+    assert max_abs(o, O_ref) <= O_TOL
+    assert max_abs(lse, L_ref) <= L_TOL
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.1, 1.0])
+def test_other_scales(fa, scale):
+    """scale = 0 (every score equal: O is the mean of the visible V rows),
+    a negative scale, and the unscaled case."""
+    x = make_inputs(1, 2, 150, 150, 64, "bf16", seed=5, device="cuda")
+    for causal in (False, True):
+        say(f"bf16 fwd scale={scale} causal={causal}")
+        o, lse = _run(fa, x, scale, causal)
+        O_ref, L_ref = oracle.dense_fwd(host(x.q), host(x.k), host(x.v), scale, causal)
+        assert max_abs(o, O_ref) <= O_TOL
+        assert max_abs(lse, L_ref) <= L_TOL
+
+
+def test_hot_rows_mid(fa):
+    """One K row per head scaled by 30: the running maximum jumps mid-row."""
+    x = make_inputs(1, 4, 700, 700, 128, "bf16", seed=8, device="cuda", hot_row_factor=30.0)
+    for causal in (False, True):
+        say(f"bf16 fwd hot rows causal={causal}")
+        o, lse = _run(fa, x, 1 / math.sqrt(128), causal)
+        O_ref, L_ref = oracle.dense_fwd(host(x.q), host(x.k), host(x.v), 1 / math.sqrt(128),
+                                        causal)
+        assert max_abs(o, O_ref) <= O_TOL
+        assert max_abs(lse, L_ref) <= L_TOL
+
+
+def test_uniform_scores_bf16(fa):
+    """q = k = 0 (d = 64): O is the mean of the visible V rows, L = ln(count)."""
+    B, H, N, d = 1, 1, 100, 64
+    z = torch.zeros((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    v = torch.arange(N, dtype=torch.float32, device="cuda").repeat_interleave(d).reshape(
+        B, H, N, d).to(torch.bfloat16)
+    say("bf16 uniform scores causal")
+    o, lse = fa.forward(z, z, v, 0.125, causal=True)
+    torch.cuda.synchronize()
+    want = np.arange(N) / 2.0  # mean of 0..i
+    np.testing.assert_allclose(host(o)[0, 0, :, 0], want, atol=O_TOL * 4, rtol=4e-3)
+    np.testing.assert_allclose(host(lse)[0, 0], np.log(np.arange(1, N + 1)), atol=L_TOL)
+
+
+def _sample_rows(B, H, Nq, n, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    rows = set(int(r) for r in rng.integers(0, B * H * Nq, n))
+    for bh in (0, B * H - 1):
+        for i in (0, 1, 63, 64, 127, 128, Nq - 1) + tuple(extra):
+            if 0 <= i < Nq:
+                rows.add(bh * Nq + i)
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name,causal", [("prefill_d64", False), ("prefill_causal_d128", True)])
+def test_full_workload_sampled(fa, name, causal):
+    say(f"bf16 fwd full workload {name}: generating")
+    x = workload_inputs(name, device="cuda")
+    B, H, Nq, d = x.q.shape
+    scale = 1 / math.sqrt(d)
+    say(f"bf16 fwd full workload {name}: running")
+    o, lse = _run(fa, x, scale, causal)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    extra = ()
+    if x.hot_rows is not None:  # rows right at and after a hot key
+        j = int(x.hot_rows[0, 0])
+        extra = (j, j + 1, min(j + 200, Nq - 1))
+    rows = _sample_rows(B, H, Nq, 400, seed=len(name), extra=extra)
+    O_ref, L_ref = oracle.dense_fwd(host(x.q), host(x.k), host(x.v), scale, causal, rows=rows)
+    got_o = host(o).reshape(-1, d)[rows]
+    got_l = host(lse).reshape(-1)[rows]
+    assert float(np.abs(got_o - O_ref).max()) <= O_TOL
+    assert float(np.abs(got_l - L_ref).max()) <= L_TOL
