@@ -1,0 +1,266 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: the non-causal prefill forward, B=4, H=16, Nq=Nk=2048,
+d=64, bf16 (one step = one fa_fwd over the whole batch, inputs resident in
+HBM).  It prints ONE JSON line whose ``value`` is that forward's throughput in
+TFLOP/s (4*B*H*Nq*Nk*d per step, halved under causal).  The same line carries
+``roofline`` for the dominant kernel, ``cpu_baseline`` (the fp64 oracle timed
+on a bounded sample on this host) and ``parts``: the causal d=128 prefill
+forward, the causal backward (10*B*H*N^2*d/2 per step) and split-KV decoding
+(GB/s of K, V, Q, O and L), each timed the same way.
+
+--workload selects another workload as the primary one.  --copy-calibration
+runs a plain device copy of known size (for scaling rocprofv3 FETCH_SIZE and
+WRITE_SIZE counters to bytes).  Only one GPU is used; --gpus N > 1 exits.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "prefill_d64": "fwd_bf16.hip", "prefill_causal_d128": "fwd_bf16.hip",
+    "bwd_causal_d64": "bwd.hip", "decode_d128": "decode.hip",
+}
+
+
+def source_hash(name: str) -> str:
+    path = os.path.join(ROOT, "flashattention_online_softmax_fa_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="prefill_d64",
+                   choices=["prefill_d64", "prefill_causal_d128", "bwd_causal_d64",
+                            "decode_d128"])
+    p.add_argument("--n-split", type=int, default=None, help="decode: splits (default best)")
+    p.add_argument("--no-parts", action="store_true", help="time only the primary workload")
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    p.add_argument("--copy-calibration", action="store_true")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# Workload runners: each returns (callable step, work units per step, unit info)
+# ---------------------------------------------------------------------------
+def setup(name, fa, torch, n_split=None):
+    from fa_inputs import WORKLOADS, workload_inputs
+    w = WORKLOADS[name]
+    x = workload_inputs(name, device="cuda")
+    B, H, Nq, d = x.q.shape
+    Nk = x.k.shape[2]
+    scale = 1.0 / math.sqrt(d)
+    causal = w["causal"][0]
+    cfg = {"workload": name, "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d, "causal": causal,
+           "dtype": "bf16"}
+    if name.startswith("prefill"):
+        o = torch.empty_like(x.q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+
+        def step():
+            fa.fa_fwd(x.q, x.k, x.v, o, lse, scale, causal)
+        flops = 4.0 * B * H * Nq * Nk * d * (0.5 if causal else 1.0)
+        return dict(step=step, work=flops, unit="TFLOP/s", bound="mfma", cfg=cfg, x=x,
+                    scale=scale, causal=causal, kernel="fwd_bf16_kernel")
+    if name.startswith("bwd"):
+        o, lse = fa.forward(x.q, x.k, x.v, scale, causal)
+        ws = torch.empty(fa.fa_bwd_workspace_size(x.q.dtype, B, H, Nq, d), dtype=torch.uint8,
+                         device="cuda")
+        dq, dk, dv = torch.empty_like(x.q), torch.empty_like(x.k), torch.empty_like(x.v)
+
+        def step():
+            fa.fa_bwd(x.q, x.k, x.v, o, lse, x.do, dq, dk, dv, ws, scale, causal)
+        flops = 10.0 * B * H * Nq * Nk * d * (0.5 if causal else 1.0)
+        return dict(step=step, work=flops, unit="TFLOP/s", bound="mfma", cfg=cfg, x=x,
+                    scale=scale, causal=causal, kernel="bwd_main_kernel",
+                    extra={"flops_no_recompute": 8.0 * B * H * Nq * Nk * d * 0.5})
+    # decode
+    splits = [n_split] if n_split else list(w["n_split"])
+    pm = {n: torch.empty((B, H, Nq, n), dtype=torch.float32, device="cuda") for n in splits}
+    pl = {n: torch.empty_like(pm[n]) for n in splits}
+    po = {n: torch.empty((B, H, Nq, n, d), dtype=torch.float32, device="cuda") for n in splits}
+    o = torch.empty_like(x.q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+    state = {"n": splits[0]}
+
+    def step():
+        n = state["n"]
+        fa.fa_decode_split(x.q, x.k, x.v, pm[n], pl[n], po[n], n, scale)
+        fa.fa_merge_states(pm[n], pl[n], po[n], o, lse)
+    bytes_ = 2.0 * (2 * B * H * Nk * d + 2 * B * H * Nq * d) + 4.0 * B * H * Nq
+    return dict(step=step, work=bytes_, unit="GB/s", bound="hbm", cfg=cfg, x=x, scale=scale,
+                causal=False, kernel="decode_split_kernel", splits=splits, state=state,
+                partial_bytes={n: 4.0 * B * H * Nq * n * (d + 2) * 2 for n in splits})
+
+
+def timed(torch, step, steps, warmup):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps  # ms per step
+
+
+def measure(run, torch, steps, warmup):
+    """Time one workload; for decode pick the fastest split count."""
+    if "splits" in run:
+        best = None
+        for n in run["splits"]:
+            run["state"]["n"] = n
+            ms = timed(torch, run["step"], steps, warmup)
+            if best is None or ms < best[0]:
+                best = (ms, n)
+        run["state"]["n"] = best[1]
+        run["cfg"]["n_split"] = best[1]
+        return best[0]
+    return timed(torch, run["step"], steps, warmup)
+
+
+def rate(run, ms):
+    scale = 1e9 if run["unit"] == "TFLOP/s" else 1e6  # work per ms -> T or G per s
+    return run["work"] / ms / scale
+
+
+def roofline(run, ms, name):
+    achieved = rate(run, ms)
+    peak = PEAK_BF16_TFLOPS if run["bound"] == "mfma" else PEAK_HBM_GBS
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f).get(name)
+        if t and t.get("source_hash") == source_hash(KERNEL_SOURCES[name]):
+            traffic = t["bytes_per_launch"]
+    except (OSError, ValueError):
+        pass
+    return {"bound": run["bound"], "achieved": round(achieved, 2), "peak": peak,
+            "unit": run["unit"] if run["bound"] == "mfma" else "GB/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "kernel": run["kernel"], "launch_ms": round(ms, 5)}
+
+
+def cpu_baseline(run, budget_s=12.0):
+    """The fp64 oracle (dense definition) on a bounded sample of query rows of
+    the same inputs, in the metric's unit."""
+    import numpy as np
+    import oracle
+    from fa_inputs import to_f64_numpy
+    x = run["x"]
+    B, H, Nq, d = x.q.shape
+    Nk = x.k.shape[2]
+    Q, K, V = (to_f64_numpy(t) for t in (x.q, x.k, x.v))
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(0)
+    total = B * H * Nq
+    n = min(total, 256)
+    spent = 0.0
+    work = 0.0
+    while True:
+        rows = np.sort(rng.choice(total, size=n, replace=False))
+        t0 = time.perf_counter()
+        oracle.dense_fwd(Q, K, V, run["scale"], run["causal"], rows=rows, nthreads=threads)
+        dt = time.perf_counter() - t0
+        if run["causal"]:
+            vis = np.minimum(rows % Nq + 1, Nk)
+        else:
+            vis = np.full(rows.shape, Nk)
+        work = float(4.0 * d * vis.sum())
+        spent = dt
+        if dt > budget_s / 4 or n == total:
+            break
+        n = int(min(total, n * max(2.0, budget_s / 2 / max(dt, 1e-3))))
+    value = work / spent / 1e12
+    return {"value": round(value, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {total} query rows (dense fp64 definition), {spent:.2f} s"}
+
+
+def copy_calibration(torch):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    n = 1 << 28  # 256 Mi fp32 = 1 GiB read + 1 GiB written
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(every (batch, head) is independent, see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import flashattention_online_softmax_fa_amd as fa
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    run = setup(args.workload, fa, torch, args.n_split)
+    ms = measure(run, torch, args.steps, args.warmup)
+    value = rate(run, ms)
+    line = {
+        "metric": "attention TFLOP/s and % of bf16 MFMA peak (fwd/bwd); decode GB/s % HBM peak",
+        "value": round(value, 3),
+        "unit": run["unit"] if run["unit"] == "TFLOP/s" else "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": run["cfg"],
+        "roofline": roofline(run, ms, args.workload),
+    }
+    if "partial_bytes" in run:
+        line["config"]["partial_state_bytes"] = run["partial_bytes"][run["state"]["n"]]
+    if "extra" in run:
+        line["config"].update(run["extra"])
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(run) if run["unit"] == "TFLOP/s" else None
+    primary_x = run.pop("x")
+    del primary_x
+    if not args.no_parts:
+        parts = {}
+        for name in ("prefill_d64", "prefill_causal_d128", "bwd_causal_d64", "decode_d128"):
+            if name == args.workload:
+                continue
+            r = setup(name, fa, torch)
+            steps = max(3, args.steps // 2) if name == "decode_d128" else args.steps
+            pms = measure(r, torch, steps, min(args.warmup, 3))
+            rf = roofline(r, pms, name)
+            parts[name] = {"ms": round(pms, 5), "value": round(rate(r, pms), 3),
+                           "unit": rf["unit"], "frac": rf["frac"], "traffic": rf["traffic"],
+                           "config": r["cfg"]}
+            if "partial_bytes" in r:
+                parts[name]["partial_state_bytes"] = r["partial_bytes"][r["state"]["n"]]
+            del r
+            torch.cuda.empty_cache()
+        line["parts"] = parts
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
