@@ -1,28 +1,34 @@
 // bwd.hip -- attention backward on bf16 matrix cores (gfx950), d in {64, 128}.
 //
 // Source: flash_backward (attention_kernels.py): D = rowsum(dO * O) first;
-// then every key/value tile is independent and walks the query tiles that
-// can see it, recomputing P = exp(S - L) from the stored L, and forms
+// then P = exp(S - L) is recomputed tile by tile from the stored L, and
 //     dV_j += P^T dO_i,  dP = dO_i V_j^T,  dS = P * (dP - D_i),
-//     dK_j += scale dS^T Q_i,  dQ_i += scale dS K_j,
-// where the dQ contributions of all key tiles are summed with atomic adds.
+//     dK_j += scale dS^T Q_i,  dQ_i += scale dS K_j.
+// The page sums dQ across key tiles with atomic adds.  Here the atomics are
+// replaced by a second, query-major pass that recomputes S and dP for its
+// own query tile and accumulates dQ in registers: on this chip fp32 atomics
+// from many workgroups travel to the memory fabric (about 0.55 GB of atomic
+// traffic per call at 2 x 16 heads x 4096 tokens), which costs more than
+// recomputing two of the five products.  The result is also deterministic.
 //
 // Three launches on the caller's stream:
-//   bwd_pre_kernel     D = rowsum(dO * O) in fp32 and dQ_acc = 0;
-//   bwd_main_kernel    one workgroup per (batch*head, 128-key tile), 4 waves of
-//                      32 keys; K and V of the wave stay in registers;
-//   dq_convert_kernel  dQ = bf16(dQ_acc).
+//   bwd_pre_kernel   D = rowsum(dO * O) in fp32;
+//   bwd_dkdv_kernel  one workgroup per (batch*head, 128-key tile), 4 waves of 32
+//                    keys, K and V in registers; walks the query tiles that can
+//                    see its keys; writes dK, dV;
+//   bwd_dq_kernel    one workgroup per (batch*head, 128-query tile), 4 waves of
+//                    32 queries, Q and dO in registers; walks the key tiles its
+//                    queries can see; writes dQ.
 //
-// Layout choices (v_mfma_f32_32x32x16_bf16, C[m][n] with lane = n):
-//   S = Q K^T and dP = dO V^T put one KEY per lane (16 queries per lane), so
-//   P and dS in registers are directly the B operands of dV^T = dO^T P and
-//   dK^T = Q^T dS.  The transposed operands dO^T and Q^T are read from the
-//   row-major LDS tiles with ds_read_b64_tr_b16: within each 16-lane group,
-//   lane i receives element i%4 of the 8-byte pieces addressed by lanes
-//   i/4 + 4t (t = 0..3), so lanes that address a 4-row x 16-column block
-//   receive its columns.  dS goes through LDS once, [key][query], for
-//   dQ = dS K, whose output has one d column per lane and makes the atomic
-//   adds contiguous.
+// Layouts (v_mfma_f32_32x32x16_bf16, C[m][n] with lane = n):
+//   dkdv: S = Q K^T and dP = dO V^T put one KEY per lane, so P and dS are
+//         directly the B operands of dV^T = dO^T P and dK^T = Q^T dS.
+//   dq:   S^T = K Q^T and dP^T = V dO^T put one QUERY per lane, so dS^T is
+//         directly the B operand of dQ^T = K^T dS^T, and L, D are per-lane.
+//   The transposed operands (dO^T, Q^T, K^T) are read from row-major LDS tiles
+//   with ds_read_b64_tr_b16: within each 16-lane group, lane i receives
+//   element i%4 of the 8-byte pieces addressed by lanes i/4 + 4t (t = 0..3),
+//   so lanes that address a 4-row x 16-column block receive its columns.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -32,8 +38,6 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
-constexpr int kKW = 32;               // keys per wave
-constexpr int kBC = kWaves * kKW;     // keys per workgroup
 constexpr int kThreads = kWaves * 64;
 
 // Transposed read of a 4-row x 16-column block of a row-major bf16 LDS tile
@@ -51,14 +55,29 @@ __device__ __forceinline__ bf16x8 join(u32x2 a, u32x2 b) {
     return __builtin_bit_cast(bf16x8, w);
 }
 
+// Eight fp32 accumulator registers r0..r0+7 -> bf16x8 (round to nearest even).
+__device__ __forceinline__ bf16x8 pack8(const f32x16 &v, int r0) {
+    const u32x4 w = {pack_bf16x2(v[r0 + 0], v[r0 + 1]), pack_bf16x2(v[r0 + 2], v[r0 + 3]),
+                     pack_bf16x2(v[r0 + 4], v[r0 + 5]), pack_bf16x2(v[r0 + 6], v[r0 + 7])};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+// 16-byte row chunk `col8` of row `row` (< rows), or zeros past the end; the
+// address is clamped so the load itself is always in bounds.
+__device__ __forceinline__ u32x4 load_row16(const uint16_t *base, int64_t row, int64_t rows,
+                                            int D, int col8) {
+    const int64_t r = row < rows ? row : rows - 1;
+    const u32x4 w = *(const u32x4 *)(base + r * D + col8 * 8);
+    return row < rows ? w : u32x4{0u, 0u, 0u, 0u};
+}
+
 // ---------------------------------------------------------------------------
-// D = rowsum(dO * O) (fp32), and zero the fp32 dQ accumulator.
+// D = rowsum(dO * O) (fp32).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict__ O,
                                                       const uint16_t *__restrict__ dO,
-                                                      float *__restrict__ Dv,
-                                                      float *__restrict__ dQacc, int64_t rows) {
+                                                      float *__restrict__ Dv, int64_t rows) {
     constexpr int LPR = D / 8;  // lanes per row (16-byte chunks)
     const int64_t chunk = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t row = chunk / LPR;
@@ -72,9 +91,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
             s = fmaf(bf16_lo(o[w]), bf16_lo(g[w]), s);
             s = fmaf(bf16_hi(o[w]), bf16_hi(g[w]), s);
         }
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        *(f32x4 *)(dQacc + row * D + sub * 8) = z;
-        *(f32x4 *)(dQacc + row * D + sub * 8 + 4) = z;
     }
     // sum over the LPR lanes of the row (aligned groups of 8 or 16 lanes)
 #pragma unroll
@@ -83,55 +99,38 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
 }
 
 // ---------------------------------------------------------------------------
-// dQ = bf16(dQ_acc), 8 elements per thread.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void dq_convert_kernel(const float *__restrict__ acc,
-                                                         uint16_t *__restrict__ dQ, int64_t n8) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n8) return;
-    const f32x4 a = *(const f32x4 *)(acc + i * 8);
-    const f32x4 b = *(const f32x4 *)(acc + i * 8 + 4);
-    const u32x4 w = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
-                     pack_bf16x2(b[2], b[3])};
-    *(u32x4 *)(dQ + i * 8) = w;
-}
-
-// ---------------------------------------------------------------------------
-// Main backward kernel.
+// dK, dV: key-major.
 // ---------------------------------------------------------------------------
 template <int D>
-struct BwdTile {
+struct DkdvTile {
+    static constexpr int KEYS = 32 * kWaves;    // keys per workgroup
     static constexpr int QB = D == 64 ? 2 : 1;  // 32-query blocks per query tile
     static constexpr int BR = 32 * QB;          // queries per query tile
-    static constexpr int RS = D + 8;            // row stride of Q, dO, K tiles in LDS
-    static constexpr int SS = BR + 8;           // row stride of the dS tile
+    static constexpr int RS = D + 8;            // LDS row stride (elements)
     static constexpr int QCH = BR * D / 8 / kThreads;  // 16-byte chunks per thread per tensor
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void bwd_main_kernel(
-    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
-    const float *__restrict__ L, const float *__restrict__ Dv, float *__restrict__ dQacc,
-    uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int64_t Nq, int64_t Nk, int nkt,
-    float scale, float c) {
-    using T = BwdTile<D>;
-    constexpr int QB = T::QB, BR = T::BR, RS = T::RS, SS = T::SS;
-    __shared__ __attribute__((aligned(16))) uint16_t sK[kBC * RS];
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[BR * RS];
-    __shared__ __attribute__((aligned(16))) uint16_t sdO[BR * RS];
-    __shared__ __attribute__((aligned(16))) uint16_t sdS[kBC * SS];
-    __shared__ __attribute__((aligned(16))) float sL[BR];
-    __shared__ __attribute__((aligned(16))) float sD[BR];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, 2)))
+void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+                     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
+                     const float *__restrict__ L, const float *__restrict__ Dv,
+                     uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int64_t Nq, int64_t Nk,
+                     int nkt, float scale, float c) {
+    using T = DkdvTile<D>;
+    constexpr int QB = T::QB, BR = T::BR, RS = T::RS;
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BR * RS];
+    __shared__ __attribute__((aligned(16))) uint16_t sdO[2][BR * RS];
+    __shared__ __attribute__((aligned(16))) float sL[2][BR];
+    __shared__ __attribute__((aligned(16))) float sD[2][BR];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 5, lr = lane & 31, s16 = lane & 15, G = lane >> 4;
     const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = lid / nkt;
     const int kt = (int)(lid % nkt);  // causal: low key tiles see the most queries; go first
-    const int64_t k0 = (int64_t)kt * kBC;
-    const int64_t kw0 = k0 + wave * kKW;
+    const int64_t k0 = (int64_t)kt * T::KEYS;
+    const int64_t kw0 = k0 + wave * 32;
     const int64_t mykey = kw0 + lr;
     const uint16_t *Qh = Q + bh * Nq * D;
     const uint16_t *dOh = dO + bh * Nq * D;
@@ -139,27 +138,13 @@ void bwd_main_kernel(
     const uint16_t *Vh = V + bh * Nk * D;
     const float *Lh = L + bh * Nq;
     const float *Dh = Dv + bh * Nq;
-    float *dQh = dQacc + bh * Nq * D;
 
-    // K and V of this wave's keys as B operands of S = Q K^T and dP = dO V^T.
+    // K and V of this wave's keys: B operands of S = Q K^T and dP = dO V^T
     bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) {
-        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-        if (mykey < Nk) {
-            a = *(const u32x4 *)(Kh + mykey * D + ds * 16 + g * 8);
-            b = *(const u32x4 *)(Vh + mykey * D + ds * 16 + g * 8);
-        }
-        kf[ds] = __builtin_bit_cast(bf16x8, a);
-        vf[ds] = __builtin_bit_cast(bf16x8, b);
-    }
-    // the workgroup's K tile in LDS, row-major, for dQ = dS K
-    for (int cidx = tid; cidx < kBC * D / 8; cidx += kThreads) {
-        const int row = cidx / (D / 8), col = cidx % (D / 8);
-        const int64_t key = k0 + row;
-        const u32x4 w = key < Nk ? *(const u32x4 *)(Kh + key * D + col * 8)
-                                 : u32x4{0u, 0u, 0u, 0u};
-        *(u32x4 *)(&sK[row * RS + col * 8]) = w;
+        kf[ds] = __builtin_bit_cast(bf16x8, load_row16(Kh, mykey, Nk, D, ds * 2 + g));
+        vf[ds] = __builtin_bit_cast(bf16x8, load_row16(Vh, mykey, Nk, D, ds * 2 + g));
     }
 
     f32x16 dvacc[D / 32], dkacc[D / 32];
@@ -183,45 +168,42 @@ void bwd_main_kernel(
         for (int u = 0; u < T::QCH; ++u) {
             const int cidx = tid + kThreads * u;
             const int row = cidx / (D / 8), col = cidx % (D / 8);
-            const int64_t q = q0 + row;
-            qreg[u] = q < Nq ? *(const u32x4 *)(Qh + q * D + col * 8) : u32x4{0u, 0u, 0u, 0u};
-            oreg[u] = q < Nq ? *(const u32x4 *)(dOh + q * D + col * 8) : u32x4{0u, 0u, 0u, 0u};
+            qreg[u] = load_row16(Qh, q0 + row, Nq, D, col);
+            oreg[u] = load_row16(dOh, q0 + row, Nq, D, col);
         }
         if (tid < BR) {
             const int64_t q = q0 + tid;
+            const int64_t qc = q < Nq ? q : Nq - 1;
             // a padded query row gets L = +inf, so its P is exactly 0
-            lreg = q < Nq ? Lh[q] * kLog2e : INFINITY;
-            dreg = q < Nq ? Dh[q] : 0.f;
+            lreg = q < Nq ? Lh[qc] * kLog2e : INFINITY;
+            dreg = q < Nq ? Dh[qc] : 0.f;
         }
     };
-    auto store_q = [&]() {
+    auto store_q = [&](int buf) {
 #pragma unroll
         for (int u = 0; u < T::QCH; ++u) {
             const int cidx = tid + kThreads * u;
             const int row = cidx / (D / 8), col = cidx % (D / 8);
-            *(u32x4 *)(&sQ[row * RS + col * 8]) = qreg[u];
-            *(u32x4 *)(&sdO[row * RS + col * 8]) = oreg[u];
+            *(u32x4 *)(&sQ[buf][row * RS + col * 8]) = qreg[u];
+            *(u32x4 *)(&sdO[buf][row * RS + col * 8]) = oreg[u];
         }
         if (tid < BR) {
-            sL[tid] = lreg;
-            sD[tid] = dreg;
+            sL[buf][tid] = lreg;
+            sD[buf][tid] = dreg;
         }
     };
 
     if (it0 < nqt) {
         load_q(it0);
-        store_q();
+        store_q(0);
     }
     __syncthreads();
 
-    // dQ output block of this wave: (query block, 32-column block)
-    const int oqb = D == 64 ? (wave >> 1) : 0;
-    const int odb = D == 64 ? (wave & 1) : wave;
-
     for (int it = it0; it < nqt; ++it) {
+        const int buf = (it - it0) & 1;
         const int64_t q0 = (int64_t)it * BR;
         if (it + 1 < nqt) load_q(it + 1);
-        const bool active = mykey - lr < Nk && (!CAUSAL || q0 + BR - 1 >= kw0);
+        const bool active = kw0 < Nk && (!CAUSAL || q0 + BR - 1 >= kw0);
         if (active) {
             // ---- S = Q K^T and dP = dO V^T (lane: key lr; register r: query
             //      8*(r/4) + 4g + r%4 of the 32-query block)
@@ -236,8 +218,8 @@ void bwd_main_kernel(
 #pragma unroll
                 for (int ds = 0; ds < D / 16; ++ds) {
                     const int off = (qb * 32 + lr) * RS + ds * 16 + g * 8;
-                    const bf16x8 aq = *(const bf16x8 *)(&sQ[off]);
-                    const bf16x8 ao = *(const bf16x8 *)(&sdO[off]);
+                    const bf16x8 aq = *(const bf16x8 *)(&sQ[buf][off]);
+                    const bf16x8 ao = *(const bf16x8 *)(&sdO[buf][off]);
                     sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ds], sacc[qb], 0, 0,
                                                                        0);
                     pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[ds], pacc[qb], 0, 0,
@@ -245,98 +227,48 @@ void bwd_main_kernel(
                 }
             }
             // ---- P = exp2(S c - L log2 e), dS = P (dP - D)
+            const bool need_mask = (kw0 + 32 > Nk) || (CAUSAL && q0 < kw0 + 31);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
                     const int qi = qb * 32 + 8 * r4 + 4 * g;
-                    const f32x4 lv = *(const f32x4 *)(&sL[qi]);
-                    const f32x4 dv = *(const f32x4 *)(&sD[qi]);
+                    const f32x4 lv = *(const f32x4 *)(&sL[buf][qi]);
+                    const f32x4 dv = *(const f32x4 *)(&sD[buf][qi]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * r4 + e;
                         float p = fast_exp2(fmaf(sacc[qb][r], c, -lv[e]));
-                        if (mykey >= Nk || (CAUSAL && mykey > q0 + qi + e)) p = 0.f;
+                        if (need_mask && (mykey >= Nk || (CAUSAL && mykey > q0 + qi + e)))
+                            p = 0.f;
                         sacc[qb][r] = p;
                         pacc[qb][r] = p * (pacc[qb][r] - dv[e]);
                     }
                 }
             }
-            // ---- bf16 B operands: k-step kq (16 queries) = registers 8h..8h+7 of block kq/2
-            bf16x8 pb[BR / 16], sb[BR / 16];
+            // ---- dV^T += dO^T P and dK^T += Q^T dS.  B operand (k-step kq of 16
+            //      queries) = registers 8h..8h+7 of block kq/2, so k-slot (g, e) is
+            //      query 8*(e/4) + 4g + e%4 of the step; the A operand (lane: column
+            //      32b + lane%32) is read transposed with the same slot order.
 #pragma unroll
             for (int kq = 0; kq < BR / 16; ++kq) {
-                const int qb = kq >> 1, h = kq & 1;
-                const u32x4 wp = {pack_bf16x2(sacc[qb][8 * h + 0], sacc[qb][8 * h + 1]),
-                                  pack_bf16x2(sacc[qb][8 * h + 2], sacc[qb][8 * h + 3]),
-                                  pack_bf16x2(sacc[qb][8 * h + 4], sacc[qb][8 * h + 5]),
-                                  pack_bf16x2(sacc[qb][8 * h + 6], sacc[qb][8 * h + 7])};
-                const u32x4 ws = {pack_bf16x2(pacc[qb][8 * h + 0], pacc[qb][8 * h + 1]),
-                                  pack_bf16x2(pacc[qb][8 * h + 2], pacc[qb][8 * h + 3]),
-                                  pack_bf16x2(pacc[qb][8 * h + 4], pacc[qb][8 * h + 5]),
-                                  pack_bf16x2(pacc[qb][8 * h + 6], pacc[qb][8 * h + 7])};
-                pb[kq] = __builtin_bit_cast(bf16x8, wp);
-                sb[kq] = __builtin_bit_cast(bf16x8, ws);
-                // dS to LDS as [key][query] for dQ = dS K
-                const int kr = wave * kKW + lr;
-                *(u32x2 *)(&sdS[kr * SS + kq * 16 + 4 * g]) = u32x2{ws[0], ws[1]};
-                *(u32x2 *)(&sdS[kr * SS + kq * 16 + 8 + 4 * g]) = u32x2{ws[2], ws[3]};
-            }
-            // ---- dV^T += dO^T P and dK^T += Q^T dS.  A operand: lane holds column
-            //      d = 32b + lane%32 at the 8 queries of its k-slots; slot (g, e) is
-            //      query 8*(e/4) + 4g + e%4 of the step, matching P's registers.
+                const bf16x8 pb = pack8(sacc[kq >> 1], 8 * (kq & 1));
+                const bf16x8 sb = pack8(pacc[kq >> 1], 8 * (kq & 1));
+                const int r0 = kq * 16 + 4 * g;
 #pragma unroll
-            for (int b = 0; b < D / 32; ++b) {
-                const int col = b * 32 + 16 * (G & 1);
-#pragma unroll
-                for (int kq = 0; kq < BR / 16; ++kq) {
-                    const int r0 = kq * 16 + 4 * g;
-                    const bf16x8 ao = join(tr_read(&sdO[r0 * RS + col], RS, s16),
-                                           tr_read(&sdO[(r0 + 8) * RS + col], RS, s16));
-                    const bf16x8 aq = join(tr_read(&sQ[r0 * RS + col], RS, s16),
-                                           tr_read(&sQ[(r0 + 8) * RS + col], RS, s16));
-                    dvacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[kq], dvacc[b], 0, 0,
-                                                                       0);
-                    dkacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb[kq], dkacc[b], 0, 0,
-                                                                       0);
+                for (int b = 0; b < D / 32; ++b) {
+                    const int col = b * 32 + 16 * (G & 1);
+                    const bf16x8 ao = join(tr_read(&sdO[buf][r0 * RS + col], RS, s16),
+                                           tr_read(&sdO[buf][(r0 + 8) * RS + col], RS, s16));
+                    const bf16x8 aq = join(tr_read(&sQ[buf][r0 * RS + col], RS, s16),
+                                           tr_read(&sQ[buf][(r0 + 8) * RS + col], RS, s16));
+                    dvacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb, dvacc[b], 0, 0, 0);
+                    dkacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb, dkacc[b], 0, 0, 0);
                 }
             }
-        } else {
-            // keys of an idle wave add nothing to dQ
-            const int kr = wave * kKW + lr;
-#pragma unroll
-            for (int kq = 0; kq < BR / 16; ++kq) {
-                *(u32x2 *)(&sdS[kr * SS + kq * 16 + 4 * g]) = u32x2{0u, 0u};
-                *(u32x2 *)(&sdS[kr * SS + kq * 16 + 8 + 4 * g]) = u32x2{0u, 0u};
-            }
         }
-        __syncthreads();  // dS complete; Q/dO tile no longer read
-        if (it + 1 < nqt) store_q();
-        // ---- dQ (32 queries x 32 columns per wave) += scale * dS K over the 128 keys.
-        //      k-slot (g, e) is key 16*ks + 8g + e in both operands.
-        {
-            f32x16 qacc;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) qacc[r] = 0.f;
-            const int qcol = oqb * 32 + 16 * (G & 1);
-            const int dcol = odb * 32 + 16 * (G & 1);
-#pragma unroll
-            for (int ks = 0; ks < kBC / 16; ++ks) {
-                const int r0 = ks * 16 + 8 * g;
-                const bf16x8 a = join(tr_read(&sdS[r0 * SS + qcol], SS, s16),
-                                      tr_read(&sdS[(r0 + 4) * SS + qcol], SS, s16));
-                const bf16x8 b = join(tr_read(&sK[r0 * RS + dcol], RS, s16),
-                                      tr_read(&sK[(r0 + 4) * RS + dcol], RS, s16));
-                qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, qacc, 0, 0, 0);
-            }
-            // lane: column odb*32 + lr; register r: query 8*(r/4) + 4g + r%4 of block oqb
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t q = q0 + oqb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                if (q < Nq) atomicAdd(dQh + q * D + odb * 32 + lr, scale * qacc[r]);
-            }
-        }
-        __syncthreads();  // next Q/dO tile visible; dS reads done
+        if (it + 1 < nqt) store_q(buf ^ 1);
+        __syncthreads();
     }
 
     // ---- epilogue: dK = scale * dK_acc, dV = dV_acc (lane: key lr; register r:
@@ -360,14 +292,176 @@ void bwd_main_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// dQ: query-major.
+// ---------------------------------------------------------------------------
+constexpr int kDqBR = 32 * kWaves;  // queries per workgroup
+constexpr int kDqBC = 64;           // keys per tile
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, 2)))
+void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+                   const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
+                   const float *__restrict__ L, const float *__restrict__ Dv,
+                   uint16_t *__restrict__ dQ, int64_t Nq, int64_t Nk, int nqt, float scale,
+                   float c) {
+    constexpr int RS = D + 8;
+    constexpr int KCH = kDqBC * D / 8 / kThreads;  // 16-byte chunks per thread per tensor
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kDqBC * RS];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][kDqBC * RS];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int g = lane >> 5, lr = lane & 31, s16 = lane & 15, G = lane >> 4;
+    const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = lid / nqt;
+    int qt = (int)(lid % nqt);
+    if (CAUSAL) qt = nqt - 1 - qt;  // heaviest query tiles first
+    const int64_t q0 = (int64_t)qt * kDqBR;
+    const int64_t qw0 = q0 + wave * 32;
+    const int64_t qrow = qw0 + lr;
+    const uint16_t *Kh = K + bh * Nk * D;
+    const uint16_t *Vh = V + bh * Nk * D;
+
+    int64_t nkt = (Nk + kDqBC - 1) / kDqBC;
+    if (CAUSAL) {
+        const int64_t qlast = (q0 + kDqBR < Nq ? q0 + kDqBR : Nq) - 1;
+        const int64_t lim = qlast / kDqBC + 1;
+        nkt = nkt < lim ? nkt : lim;
+    }
+    const int64_t qw_last = (qw0 + 31 < Nq - 1) ? qw0 + 31 : Nq - 1;
+
+    // Q and dO of this lane's query: B operands of S^T = K Q^T and dP^T = V dO^T
+    bf16x8 qf[D / 16], of[D / 16];
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+        qf[ds] = __builtin_bit_cast(bf16x8, load_row16(Q + bh * Nq * D, qrow, Nq, D, ds * 2 + g));
+        of[ds] = __builtin_bit_cast(bf16x8, load_row16(dO + bh * Nq * D, qrow, Nq, D, ds * 2 + g));
+    }
+    const int64_t qc = qrow < Nq ? qrow : Nq - 1;
+    const float l2 = qrow < Nq ? L[bh * Nq + qc] * kLog2e : INFINITY;  // padded row: P = 0
+    const float dq = qrow < Nq ? Dv[bh * Nq + qc] : 0.f;
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
+
+    u32x4 kreg[KCH], vreg[KCH];
+    auto load_kv = [&](int64_t j) {
+        const int64_t kv0 = j * kDqBC;
+#pragma unroll
+        for (int u = 0; u < KCH; ++u) {
+            const int cidx = tid + kThreads * u;
+            const int row = cidx / (D / 8), col = cidx % (D / 8);
+            kreg[u] = load_row16(Kh, kv0 + row, Nk, D, col);
+            vreg[u] = load_row16(Vh, kv0 + row, Nk, D, col);
+        }
+    };
+    auto store_kv = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < KCH; ++u) {
+            const int cidx = tid + kThreads * u;
+            const int row = cidx / (D / 8), col = cidx % (D / 8);
+            *(u32x4 *)(&sK[buf][row * RS + col * 8]) = kreg[u];
+            *(u32x4 *)(&sV[buf][row * RS + col * 8]) = vreg[u];
+        }
+    };
+
+    load_kv(0);
+    store_kv(0);
+    __syncthreads();
+
+    for (int64_t j = 0; j < nkt; ++j) {
+        const int buf = (int)(j & 1);
+        if (j + 1 < nkt) load_kv(j + 1);
+        const int64_t kv0 = j * kDqBC;
+        const bool active = qw0 < Nq && (!CAUSAL || kv0 <= qw_last);
+        if (active) {
+            // ---- S^T = K Q^T, dP^T = V dO^T (lane: query lr; register r: key
+            //      8*(r/4) + 4g + r%4 of the 32-key block)
+            f32x16 sacc[kDqBC / 32], pacc[kDqBC / 32];
+#pragma unroll
+            for (int kb = 0; kb < kDqBC / 32; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    sacc[kb][r] = 0.f;
+                    pacc[kb][r] = 0.f;
+                }
+#pragma unroll
+                for (int ds = 0; ds < D / 16; ++ds) {
+                    const int off = (kb * 32 + lr) * RS + ds * 16 + g * 8;
+                    const bf16x8 ak = *(const bf16x8 *)(&sK[buf][off]);
+                    const bf16x8 av = *(const bf16x8 *)(&sV[buf][off]);
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[ds], sacc[kb], 0, 0,
+                                                                       0);
+                    pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[ds], pacc[kb], 0, 0,
+                                                                       0);
+                }
+            }
+            // ---- P = exp2(S c - L log2 e), dS = P (dP - D), both per lane
+            const bool need_mask = (kv0 + kDqBC > Nk) || (CAUSAL && kv0 + kDqBC - 1 > qw0);
+#pragma unroll
+            for (int kb = 0; kb < kDqBC / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float p = fast_exp2(fmaf(sacc[kb][r], c, -l2));
+                    if (need_mask) {
+                        const int64_t key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                        if (key >= Nk || (CAUSAL && key > qrow)) p = 0.f;
+                    }
+                    pacc[kb][r] = p * (pacc[kb][r] - dq);
+                }
+            // ---- dQ^T += K^T dS^T.  B operand (k-step ks of 16 keys) = registers
+            //      8h..8h+7 of block ks/2: k-slot (g, e) is key 8*(e/4) + 4g + e%4 of
+            //      the step; K^T (lane: column 32b + lane%32) is read transposed in
+            //      the same slot order.
+#pragma unroll
+            for (int ks = 0; ks < kDqBC / 16; ++ks) {
+                const bf16x8 sb = pack8(pacc[ks >> 1], 8 * (ks & 1));
+                const int r0 = ks * 16 + 4 * g;
+#pragma unroll
+                for (int b = 0; b < D / 32; ++b) {
+                    const int col = b * 32 + 16 * (G & 1);
+                    const bf16x8 a = join(tr_read(&sK[buf][r0 * RS + col], RS, s16),
+                                          tr_read(&sK[buf][(r0 + 8) * RS + col], RS, s16));
+                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, acc[b], 0, 0, 0);
+                }
+            }
+        }
+        if (j + 1 < nkt) store_kv(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: dQ = scale * acc (lane: query lr; register r: column
+    //      32b + 8*(r/4) + 4g + r%4)
+    if (qrow < Nq) {
+        uint16_t *row = dQ + (bh * Nq + qrow) * D;
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const u32x2 w = {pack_bf16x2(scale * acc[b][4 * t], scale * acc[b][4 * t + 1]),
+                                 pack_bf16x2(scale * acc[b][4 * t + 2], scale * acc[b][4 * t + 3])};
+                *(u32x2 *)(row + b * 32 + 8 * t + 4 * g) = w;
+            }
+    }
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_main(const BwdArgs &a, hipStream_t s) {
-    const int nkt = (int)((a.Nk + kBC - 1) / kBC);
-    const dim3 grid((unsigned)(a.B * a.H * nkt));
-    hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, s,
-                       (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
-                       (const uint16_t *)a.dO, a.L, a.D, a.dQacc, (uint16_t *)a.dK,
+    const int nkt = (int)((a.Nk + DkdvTile<D>::KEYS - 1) / DkdvTile<D>::KEYS);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(a.B * a.H * nkt)),
+                       dim3(kThreads), 0, s, (const uint16_t *)a.Q, (const uint16_t *)a.K,
+                       (const uint16_t *)a.V, (const uint16_t *)a.dO, a.L, a.D, (uint16_t *)a.dK,
                        (uint16_t *)a.dV, a.Nq, a.Nk, nkt, a.scale, a.scale * kLog2e);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nqt = (int)((a.Nq + kDqBR - 1) / kDqBR);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(a.B * a.H * nqt)),
+                       dim3(kThreads), 0, s, (const uint16_t *)a.Q, (const uint16_t *)a.K,
+                       (const uint16_t *)a.V, (const uint16_t *)a.dO, a.L, a.D, (uint16_t *)a.dQ,
+                       a.Nq, a.Nk, nqt, a.scale, a.scale * kLog2e);
     return hipGetLastError();
 }
 
@@ -379,21 +473,14 @@ hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s) {
     const dim3 pre_grid((unsigned)((chunks + 255) / 256));
     if (a.d == 128)
         hipLaunchKernelGGL(bwd_pre_kernel<128>, pre_grid, dim3(256), 0, s, (const uint16_t *)a.O,
-                           (const uint16_t *)a.dO, a.D, a.dQacc, rows);
+                           (const uint16_t *)a.dO, a.D, rows);
     else
         hipLaunchKernelGGL(bwd_pre_kernel<64>, pre_grid, dim3(256), 0, s, (const uint16_t *)a.O,
-                           (const uint16_t *)a.dO, a.D, a.dQacc, rows);
+                           (const uint16_t *)a.dO, a.D, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.d == 128)
-        e = a.causal ? launch_main<128, true>(a, s) : launch_main<128, false>(a, s);
-    else
-        e = a.causal ? launch_main<64, true>(a, s) : launch_main<64, false>(a, s);
-    if (e != hipSuccess) return e;
-    const int64_t n8 = rows * a.d / 8;
-    hipLaunchKernelGGL(dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,
-                       a.dQacc, (uint16_t *)a.dQ, n8);
-    return hipGetLastError();
+    if (a.d == 128) return a.causal ? launch_main<128, true>(a, s) : launch_main<128, false>(a, s);
+    return a.causal ? launch_main<64, true>(a, s) : launch_main<64, false>(a, s);
 }
 
 }  // namespace fa

@@ -72,10 +72,9 @@ fa_status fa_fwd_blocked(fa_dtype dt, const void *Q, const void *K, const void *
 
 size_t fa_bwd_workspace_size(fa_dtype dt, int64_t B, int64_t H, int64_t Nq, int64_t d) {
     if (!dtype_ok(dt) || !sizes_ok(B, H, Nq, 1, d)) return 0;
+    (void)d;
     const size_t rows = (size_t)(B * H * Nq);
-    const size_t d_bytes = (rows * 4 + 255) / 256 * 256;
-    const size_t acc_bytes = (rows * (size_t)d * 4 + 255) / 256 * 256;
-    return d_bytes + acc_bytes;
+    return (rows * 4 + 255) / 256 * 256;
 }
 
 fa_status fa_bwd(fa_dtype dt, const void *Q, const void *K, const void *V, const void *O,
@@ -97,10 +96,8 @@ fa_status fa_bwd(fa_dtype dt, const void *Q, const void *K, const void *V, const
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (B * H * ((Nk + 63) / 64) > kMaxGrid || B * H * ((Nq + 63) / 64) > kMaxGrid)
         return FA_ERR_UNSUPPORTED;
-    const size_t rows = (size_t)(B * H * Nq);
-    float *D = (float *)workspace;
-    float *acc = (float *)((char *)workspace + (rows * 4 + 255) / 256 * 256);
-    fa::BwdArgs a{Q, K, V, O, dO, L, dQ, dK, dV, D, acc, B, H, Nq, Nk, d, scale, causal};
+    fa::BwdArgs a{Q, K, V, O, dO, L, dQ, dK, dV, (float *)workspace, B, H, Nq, Nk, d, scale,
+                  causal};
     return hip_status(fa::launch_bwd_bf16(a, (hipStream_t)stream));
 }
 

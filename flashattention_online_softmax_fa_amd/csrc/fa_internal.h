@@ -22,8 +22,7 @@ struct BwdArgs {
     const void *Q, *K, *V, *O, *dO;
     const float *L;
     void *dQ, *dK, *dV;
-    float *D;      // workspace [B][H][Nq]
-    float *dQacc;  // workspace [B][H][Nq][d]
+    float *D;  // workspace [B][H][Nq]
     int64_t B, H, Nq, Nk, d;
     float scale;
     int causal;

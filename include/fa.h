@@ -89,9 +89,9 @@ fa_status fa_fwd_blocked(fa_dtype dt, const void *Q, const void *K, const void *
                          float scale, int causal, int64_t kv_block, void *stream);
 
 /*
- * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs: D
- * ([B][H][Nq] fp32) and the fp32 dQ accumulator ([B][H][Nq][d]), each
- * 256-byte aligned.  Returns 0 for invalid sizes.
+ * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs: the row
+ * sums D = rowsum(dO * O), [B][H][Nq] fp32, rounded up to 256 bytes.
+ * Returns 0 for invalid sizes.
  */
 size_t fa_bwd_workspace_size(fa_dtype dt, int64_t B, int64_t H, int64_t Nq, int64_t d);
 
@@ -100,15 +100,16 @@ size_t fa_bwd_workspace_size(fa_dtype dt, int64_t B, int64_t H, int64_t Nq, int6
  * Source: flash_backward (attention_kernels.py): D = rowsum(dO * O); key/value
  * tiles are independent; each walks the query tiles, recomputes
  * P = exp(S - L) from the stored L, forms dV += P^T dO, dP = dO V^T,
- * dS = P * (dP - D), dK += scale dS^T Q, and adds scale dS K into dQ from
- * every key tile (atomic adds into an fp32 accumulator).
+ * dS = P * (dP - D), dK += scale dS^T Q and dQ += scale dS K.  dK and dV
+ * are accumulated per key tile; dQ is accumulated per query tile by a
+ * second pass that recomputes S and dP (no atomic additions), so the
+ * result is deterministic.
  *   dt         FA_BF16 only (FA_F32 returns FA_ERR_UNSUPPORTED); d in {64, 128}.
  *   O, L       the forward's outputs for the same Q, K, V, scale, causal.
  *   dO         upstream gradient [B][H][Nq][d] bf16.
  *   dQ, dK, dV outputs, bf16, fully overwritten.
  *   workspace  device buffer of at least fa_bwd_workspace_size() bytes,
  *              256-byte aligned; its contents on entry do not matter.
- * The fp32 atomic additions into dQ make its low bits depend on timing.
  */
 fa_status fa_bwd(fa_dtype dt, const void *Q, const void *K, const void *V, const void *O,
                  const float *L, const void *dO, void *dQ, void *dK, void *dV, void *workspace,

@@ -67,15 +67,14 @@ def test_hot_rows(fa):
         assert max_rel(got, g[key]) <= REL, key
 
 
-def test_repeat_calls_agree(fa):
-    """Two calls on the same inputs differ only by the order of the fp32
-    atomic additions into dQ (dK, dV are produced without atomics)."""
+def test_repeat_calls_bitwise_equal(fa):
+    """No atomics: two calls on the same inputs give identical bits."""
     x = make_inputs(1, 2, 256, 256, 64, "bf16", seed=3, device="cuda", backward=True)
     say("bwd repeat")
     a = _fwd_bwd(fa, x, 0.125, True)
     b = _fwd_bwd(fa, x, 0.125, True)
-    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
-    assert (a[0].float() - b[0].float()).abs().max().item() <= 1e-2
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
 
 
 def test_full_workload(fa):
