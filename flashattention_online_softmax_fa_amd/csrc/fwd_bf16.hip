@@ -3,69 +3,92 @@
 // Source: flash_forward (attention_kernels.py): every query tile is
 // independent; it keeps a running row maximum m, denominator l and an
 // unnormalised accumulator on chip while it walks the key/value tiles,
-// rescales them by exp(m_old - m_new) when the maximum grows, skips key
-// tiles that lie entirely after its last query under the causal mask,
-// divides once at the end and writes L = m + log l.
+// rescales them when the maximum grows, skips key tiles that lie entirely
+// after its last query under the causal mask, divides once at the end and
+// writes L = m + log l.
 //
 // Work split.  One workgroup (4 waves) per (batch*head, 128-query tile); each
-// wave owns 32 queries.  Key/value tiles of 64 keys are staged in LDS, double
-// buffered, one barrier per tile; the next tile's HBM loads are issued before
-// the current tile is computed and written to LDS after it.
+// wave owns 32 queries, whose Q rows stay in registers.  Key/value tiles of 64
+// keys stream from HBM straight into an LDS ring of STAGES slots with
+// global_load_lds_dwordx4 (no register staging); each wave issues its share of
+// a tile and waits on its own load counter, and one barrier per tile both
+// publishes the tile and frees the slot read in the previous iteration.
 //
-// Matrix-core layout (v_mfma_f32_32x32x16_bf16).  The wave computes the
-// transposed score block S^T = K Q^T, so each lane's 16 accumulator values
-// belong to ONE query (lane % 32) and 16 keys; the row maximum and sum are
-// per-lane work plus one exchange with lane ^ 32.  Those same registers,
-// rounded to bf16, are directly the B operand of O^T += V^T P^T; V^T comes from
-// LDS, where V is stored transposed (and key-permuted to match the order in
-// which P sits in the registers) when the tile is staged.  Q stays in
-// registers as the B operand of every score product.
+// LDS layout.  K and V tiles are row-major (one key per row, 16-byte chunks).
+// Chunk c of row r is stored at chunk c ^ f(r), f(r) = 2*(r%4) + (r/4)%2, which
+// makes both access patterns below free of bank conflicts: 8 lanes reading the
+// same chunk of 8 consecutive rows, and 16 lanes reading 32 bytes of 4
+// consecutive rows.
 //
-// Softmax statistics are kept in base 2: scores are multiplied by
-// scale*log2(e) inside the exponent's FMA, and L is converted back to the
-// natural logarithm at the end.
+// Matrix-core layout (v_mfma_f32_32x32x16_bf16, C[m][n] with lane = n).  The
+// wave computes S^T = K Q^T, so each lane's 16 accumulator values belong to
+// one query (lane % 32) and 16 keys; row max and sum are per-lane work.  Those
+// registers, rounded to bf16, are the B operand of O^T += V^T P^T.  V^T is
+// read from the row-major V tile with ds_read_b64_tr_b16 (within each 16-lane
+// group, lane i receives element i%4 of the 8-byte pieces addressed by lanes
+// i/4 + 4t, so lanes addressing a 4-row x 16-column block get its columns).
+//
+// Softmax statistics are base 2 with scale*log2(e) folded into the exponent's
+// FMA; L is converted back to the natural logarithm at the end.
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
 constexpr int kWaves = 4;
 constexpr int kQW = 32;                // queries per wave
 constexpr int kBR = kWaves * kQW;      // queries per workgroup
 constexpr int kBC = 64;                // keys per tile
 constexpr int kThreads = kWaves * 64;
+constexpr float kMargin = 8.f;         // base-2 headroom before the reference max is raised
 
 template <int D>
 struct Tile {
-    static constexpr int KS = D + 8;   // K row stride in LDS (elements); 16-byte rows, bank shift 4
-    static constexpr int VS = kBC + 8; // V^T row stride (elements)
-    static constexpr int KCH = kBC * D / 8 / kThreads;       // 16-byte K chunks per thread
-    static constexpr int VTASKS = (kBC / 4) * (D / 8);        // 4-key x 8-column V blocks
+    static constexpr int CH = D / 8;                 // 16-byte chunks per row
+    static constexpr int ROWB = D * 2;               // bytes per row
+    static constexpr int TILEB = kBC * ROWB;         // bytes of one K or V tile
+    static constexpr int STAGES = D == 64 ? 3 : 2;   // LDS ring depth
+    static constexpr int IPW = TILEB / 1024 / kWaves;  // 1 KiB loads per wave per tensor
+    static constexpr int RPI = 1024 / ROWB;          // rows per 1 KiB load
 };
 
-// Position of key k (k % 4 == 0, 0 <= k < kBC) in a V^T row: within each group
-// of 16 keys, keys 0-3, 8-11 come first and 4-7, 12-15 second -- the order in
-// which lane halves 0 and 1 hold P in the S^T accumulator.  16-byte chunks
-// are XOR-swizzled by row to spread the transposing stores over LDS banks.
-__device__ __forceinline__ int vt_offset(int row, int k, int VS) {
-    const int kk = k & 15;
-    const int p = (k & ~15) + ((kk >> 2) & 1) * 8 + (kk >> 3) * 4;
-    const int chunk = (p >> 3) ^ ((row >> 3) & 7);
-    return row * VS + chunk * 8 + (p & 7);
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// Wait until at most N of this wave's vector-memory operations are pending
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8; LDS operations are also drained).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// Workgroup barrier that orders LDS accesses but does not drain outstanding
+// global loads (the ring prefetch stays in flight across it).
+__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ u32x2 tr_read(const uint8_t *p) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+    return __builtin_bit_cast(u32x2, v);
 }
 
 template <int D, bool CAUSAL, bool POS_SCALE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
-    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ L, int64_t Nq,
-    int64_t Nk, int nqt, float c) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2, 3)))
+void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+                     const uint16_t *__restrict__ V, uint16_t *__restrict__ O,
+                     float *__restrict__ L, int64_t Nq, int64_t Nk, int nqt, float c) {
     using T = Tile<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBC * T::KS];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * T::VS];
+    constexpr int S = T::STAGES;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * 2 * T::TILEB];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int g = lane >> 5, lr = lane & 31;
+    const int g = lane >> 5, lr = lane & 31, s16 = lane & 15, G = lane >> 4;
+    const int xaddr = (lane ^ 32) << 2;  // ds_bpermute address of the other half of the row
     const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = lid / nqt;
     int qt = (int)(lid % nqt);
@@ -73,7 +96,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int64_t q0 = (int64_t)qt * kBR;
     const int64_t qw0 = q0 + wave * kQW;
     const int64_t qrow = qw0 + lr;
-    const uint16_t *Qh = Q + bh * Nq * D;
     const uint16_t *Kh = K + bh * Nk * D;
     const uint16_t *Vh = V + bh * Nk * D;
 
@@ -85,13 +107,58 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     const int64_t qw_last = (qw0 + kQW - 1 < Nq - 1) ? qw0 + kQW - 1 : Nq - 1;
 
-    // Q fragments: B operand of S^T = K Q^T (lane: query lr, 8 columns per 16-step)
-    bf16x8 qf[D / 16];
+    // ---- per-lane constants of the ring loads: this lane fills LDS chunk
+    //      `lane` of each of its IPW 1 KiB blocks with logical chunk
+    //      (lane % CH) ^ f(row) of that row.
+    int ld_row[T::IPW], ld_col[T::IPW];
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (qrow < Nq) w = *(const u32x4 *)(Qh + qrow * D + ds * 16 + g * 8);
-        qf[ds] = __builtin_bit_cast(bf16x8, w);
+    for (int u = 0; u < T::IPW; ++u) {
+        const int blk = wave * T::IPW + u;
+        const int row = blk * T::RPI + lane / T::CH;
+        ld_row[u] = row;
+        ld_col[u] = ((lane % T::CH) ^ swz(row)) * 8;
+    }
+    auto issue = [&](int64_t j, int st) {
+        const int64_t kv0 = j * kBC;
+        uint8_t *kb = smem + st * 2 * T::TILEB;
+        uint8_t *vb = kb + T::TILEB;
+#pragma unroll
+        for (int u = 0; u < T::IPW; ++u) {
+            int64_t key = kv0 + ld_row[u];
+            key = key < Nk ? key : Nk - 1;  // past the end: a real row, masked later
+            const int blk = wave * T::IPW + u;
+            __builtin_amdgcn_global_load_lds((const void *)(Kh + key * D + ld_col[u]),
+                                             (lds_void *)(kb + blk * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(Vh + key * D + ld_col[u]),
+                                             (lds_void *)(vb + blk * 1024), 16, 0, 0);
+        }
+    };
+
+    // ---- per-lane constants of the LDS reads
+    // K (A operand of S^T): row kb*32 + lr, logical chunk 2*ds + g
+    int koff[D / 16];
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) koff[ds] = lr * T::ROWB + 16 * ((2 * ds + g) ^ swz(lr));
+    // V^T (A operand of O^T, transposed read): rows 16ks + 4g + 8h + s/4,
+    // columns 32b + 16*(G&1) + 4*(s%4)
+    int voff[D / 32];
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) {
+        const int row = 4 * g + (s16 >> 2);
+        const int chunk = 4 * b + 2 * (G & 1) + ((s16 >> 1) & 1);
+        voff[b] = row * T::ROWB + 16 * (chunk ^ (((s16 >> 2) << 1) | g)) + 8 * (s16 & 1);
+    }
+
+    // ---- Q fragments: B operand of S^T = K Q^T (lane: query lr)
+    bf16x8 qf[D / 16];
+    {
+        const int64_t qr = qrow < Nq ? qrow : Nq - 1;
+        const uint16_t *qp = Q + (bh * Nq + qr) * D + g * 8;
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) {
+            const u32x4 w = *(const u32x4 *)(qp + ds * 16);
+            qf[ds] = __builtin_bit_cast(bf16x8, qrow < Nq ? w : u32x4{0u, 0u, 0u, 0u});
+        }
     }
 
     f32x16 oacc[D / 32];
@@ -101,148 +168,118 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
     float m = -INFINITY, l = 0.f;
 
-    u32x4 kreg[T::KCH];
-    u32x4 vreg[4];
-    const int vdoct = tid % (D / 8), vquad = tid / (D / 8);
-
-    auto load_tile = [&](int64_t j) {
-        const int64_t kv0 = j * kBC;
 #pragma unroll
-        for (int u = 0; u < T::KCH; ++u) {
-            const int cidx = tid + kThreads * u;
-            const int row = cidx / (D / 8), col = cidx % (D / 8);
-            const int64_t key = kv0 + row;
-            kreg[u] = key < Nk ? *(const u32x4 *)(Kh + key * D + col * 8) : u32x4{0u, 0u, 0u, 0u};
-        }
-        if (tid < T::VTASKS) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t key = kv0 + 4 * vquad + u;
-                vreg[u] = key < Nk ? *(const u32x4 *)(Vh + key * D + vdoct * 8)
-                                   : u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < T::KCH; ++u) {
-            const int cidx = tid + kThreads * u;
-            const int row = cidx / (D / 8), col = cidx % (D / 8);
-            *(u32x4 *)(&sK[buf][row * T::KS + col * 8]) = kreg[u];
-        }
-        if (tid < T::VTASKS) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                // column 2w: low halves of the four key rows; column 2w+1: high halves
-                const u32x2 lo = {(vreg[0][w] & 0xffffu) | (vreg[1][w] << 16),
-                                  (vreg[2][w] & 0xffffu) | (vreg[3][w] << 16)};
-                const u32x2 hi = {(vreg[0][w] >> 16) | (vreg[1][w] & 0xffff0000u),
-                                  (vreg[2][w] >> 16) | (vreg[3][w] & 0xffff0000u)};
-                const int r0 = vdoct * 8 + 2 * w;
-                *(u32x2 *)(&sV[buf][vt_offset(r0, 4 * vquad, T::VS)]) = lo;
-                *(u32x2 *)(&sV[buf][vt_offset(r0 + 1, 4 * vquad, T::VS)]) = hi;
-            }
-        }
-    };
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+    for (int t = 0; t < S - 1; ++t)
+        if (t < nkt) issue(t, t);
 
     for (int64_t j = 0; j < nkt; ++j) {
-        const int buf = (int)(j & 1);
-        if (j + 1 < nkt) load_tile(j + 1);
+        // tile j has landed for this wave once only the loads issued after it
+        // (tiles j+1 .. j+S-2) may still be pending
+        if (S == 3 && j + 1 < nkt)
+            wait_vm<2 * T::IPW>();
+        else
+            wait_vm<0>();
+        lds_barrier();
+        if (j + S - 1 < nkt) issue(j + S - 1, (int)((j + S - 1) % S));
+        const uint8_t *kbase = smem + (j % S) * 2 * T::TILEB;
+        const uint8_t *vbase = kbase + T::TILEB;
         const int64_t kv0 = j * kBC;
         const bool active = qw0 < Nq && (!CAUSAL || kv0 <= qw_last);
-        if (active) {
-            // ---- S^T = K_j Q^T
-            f32x16 sacc[kBC / 32];
+        if (!active) continue;
+
+        // ---- S^T = K_j Q^T
+        f32x16 sacc[kBC / 32];
 #pragma unroll
-            for (int kb = 0; kb < kBC / 32; ++kb) {
+        for (int kb = 0; kb < kBC / 32; ++kb) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
-                for (int ds = 0; ds < D / 16; ++ds) {
-                    const bf16x8 a = *(const bf16x8 *)(&sK[buf][(kb * 32 + lr) * T::KS +
-                                                               ds * 16 + g * 8]);
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], sacc[kb], 0, 0,
-                                                                       0);
-                }
-            }
-            if (!POS_SCALE) {
-#pragma unroll
-                for (int kb = 0; kb < kBC / 32; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sacc[kb][r] *= c;
-            }
-            // ---- mask: keys past Nk, and keys after the query under causal
-            const bool need_mask = (kv0 + kBC > Nk) || (CAUSAL && kv0 + kBC - 1 > qw0);
-            if (need_mask) {
-#pragma unroll
-                for (int kb = 0; kb < kBC / 32; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int64_t key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                        if (key >= Nk || (CAUSAL && key > qrow)) sacc[kb][r] = -INFINITY;
-                    }
-            }
-            // ---- online softmax (base 2)
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < kBC / 32; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m, POS_SCALE ? mx * c : mx);
-            const float mref = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m - mref);
-            float lsum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < kBC / 32; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = fast_exp2(POS_SCALE ? fmaf(sacc[kb][r], c, -mref)
-                                                        : sacc[kb][r] - mref);
-                    sacc[kb][r] = p;
-                    lsum += p;
-                }
-            l = l * alpha + lsum;  // per-lane partial: this lane's 32 of the tile's 64 keys
-            if (__any(m_new != m)) {
-#pragma unroll
-                for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
-            }
-            m = m_new;
-            // ---- P^T as bf16 B operands: k-step ks uses registers 8h..8h+7 of block ks/2
-            bf16x8 pf[kBC / 16];
-#pragma unroll
-            for (int ks = 0; ks < kBC / 16; ++ks) {
-                const int kb = ks >> 1, h = ks & 1;
-                const u32x4 w = {pack_bf16x2(sacc[kb][8 * h + 0], sacc[kb][8 * h + 1]),
-                                 pack_bf16x2(sacc[kb][8 * h + 2], sacc[kb][8 * h + 3]),
-                                 pack_bf16x2(sacc[kb][8 * h + 4], sacc[kb][8 * h + 5]),
-                                 pack_bf16x2(sacc[kb][8 * h + 6], sacc[kb][8 * h + 7])};
-                pf[ks] = __builtin_bit_cast(bf16x8, w);
-            }
-            // ---- O^T += V_j^T P^T
-#pragma unroll
-            for (int b = 0; b < D / 32; ++b) {
-                const int row = b * 32 + lr;
-#pragma unroll
-                for (int ks = 0; ks < kBC / 16; ++ks) {
-                    const int chunk = (ks * 2 + g) ^ ((row >> 3) & 7);
-                    const bf16x8 a = *(const bf16x8 *)(&sV[buf][row * T::VS + chunk * 8]);
-                    oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], oacc[b], 0, 0, 0);
-                }
+            for (int ds = 0; ds < D / 16; ++ds) {
+                const bf16x8 a = *(const bf16x8 *)(kbase + kb * 32 * T::ROWB + koff[ds]);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], sacc[kb], 0, 0, 0);
             }
         }
-        if (j + 1 < nkt) store_tile(buf ^ 1);
-        __syncthreads();
+        if (!POS_SCALE) {
+#pragma unroll
+            for (int kb = 0; kb < kBC / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[kb][r] *= c;
+        }
+        // ---- mask: keys past Nk, and keys after the query under causal.  Key
+        //      offset of register r in this lane: kb*32 + 8*(r/4) + 4g + r%4.
+        const bool need_mask = (kv0 + kBC > Nk) || (CAUSAL && kv0 + kBC - 1 > qw0);
+        if (need_mask) {
+            int64_t lim64 = Nk - 1 - kv0;  // last visible key offset
+            if (CAUSAL && qrow - kv0 < lim64) lim64 = qrow - kv0;
+            const int lim = (int)(lim64 < -1 ? -1 : (lim64 > kBC ? kBC : lim64)) - 4 * g;
+#pragma unroll
+            for (int kb = 0; kb < kBC / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
+        }
+        // ---- online softmax (base 2).  m is a reference maximum: it is raised
+        //      (and the accumulator rescaled) only when the tile maximum exceeds it
+        //      by more than kMargin, so exponents stay <= 2^kMargin and most tiles
+        //      skip the rescale.  O = acc / l and L = m + log2 l do not depend on
+        //      which reference is used.
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < kBC / 32; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[kb][r], sacc[kb][r + 1]));
+        // this lane's half of the tile; the other half of the row is in lane ^ 32
+        const float mt = POS_SCALE ? mx * c : mx;
+        if (__any(mt > m + kMargin)) {
+            const float mj = fmaxf(mt, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                                    xaddr, __builtin_bit_cast(int, mt))));
+            const bool grow = mj > m + kMargin;  // same in both lanes of the row
+            const float m_new = grow ? mj : m;
+            const float alpha = fast_exp2(m - m_new);  // 0 on the first tile, else <= 1
+            l *= alpha;
+#pragma unroll
+            for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+            m = m_new;
+        }
+        const float mref = (m == -INFINITY) ? 0.f : m;
+        // ---- P^T as bf16 B operands: k-step ks uses registers 8h..8h+7 of block ks/2,
+        //      so k-slot (g, e) is key 8*(e/4) + 4g + e%4 of the step
+        bf16x8 pf[kBC / 16];
+        float lsum = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < kBC / 16; ++ks) {
+            const int kb = ks >> 1, h = ks & 1;
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p[e] = fast_exp2(POS_SCALE ? fmaf(sacc[kb][8 * h + e], c, -mref)
+                                           : sacc[kb][8 * h + e] - mref);
+                lsum += p[e];
+            }
+            const u32x4 w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                             pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+            pf[ks] = __builtin_bit_cast(bf16x8, w);
+        }
+        l += lsum;  // this lane's half of the tile's keys
+        // ---- O^T += V_j^T P^T; V^T read transposed in the same k-slot order
+#pragma unroll
+        for (int ks = 0; ks < kBC / 16; ++ks) {
+#pragma unroll
+            for (int b = 0; b < D / 32; ++b) {
+                const uint8_t *p = vbase + voff[b] + ks * 16 * T::ROWB;
+                const u32x2 lo = tr_read(p), hi = tr_read(p + 8 * T::ROWB);
+                const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+                oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, w), pf[ks], oacc[b], 0, 0, 0);
+            }
+        }
     }
 
     // ---- epilogue: one division, natural-log L
-    const float l_tot = l + __shfl_xor(l, 32);
+    const float l_tot = l + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                    xaddr, __builtin_bit_cast(int, l)));
     if (qrow < Nq) {
         const float inv = 1.f / l_tot;
         uint16_t *orow = O + (bh * Nq + qrow) * D;
