@@ -33,6 +33,15 @@
 #include "fa_device.h"
 #include "fa_internal.h"
 
+#ifndef FA_FWD_QB64
+#define FA_FWD_QB64 2
+#define FA_FWD_BC64 64
+#define FA_FWD_ST64 2
+#define FA_FWD_QB128 1
+#define FA_FWD_BC128 32
+#define FA_FWD_ST128 2
+#endif
+
 namespace fa {
 namespace {
 
@@ -41,20 +50,24 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 4;
-constexpr int kQW = 32;                // queries per wave
-constexpr int kBR = kWaves * kQW;      // queries per workgroup
-constexpr int kBC = 64;                // keys per tile
 constexpr int kThreads = kWaves * 64;
 constexpr float kMargin = 8.f;         // base-2 headroom before the reference max is raised
 
-template <int D>
+// D: head dimension; QB: 32-query blocks per wave (each K / V^T fragment read
+// from LDS feeds QB matrix-core products); BC: keys per tile.
+template <int D, int QB, int BC_, int STAGES_>
 struct Tile {
+    static constexpr int BC = BC_;
+    static constexpr int QW = 32 * QB;               // queries per wave
+    static constexpr int BR = kWaves * QW;           // queries per workgroup
     static constexpr int CH = D / 8;                 // 16-byte chunks per row
     static constexpr int ROWB = D * 2;               // bytes per row
-    static constexpr int TILEB = kBC * ROWB;         // bytes of one K or V tile
-    static constexpr int STAGES = D == 64 ? 3 : 2;   // LDS ring depth
+    static constexpr int TILEB = BC * ROWB;          // bytes of one K or V tile
+    static constexpr int STAGES = STAGES_;           // LDS ring depth
     static constexpr int IPW = TILEB / 1024 / kWaves;  // 1 KiB loads per wave per tensor
     static constexpr int RPI = 1024 / ROWB;          // rows per 1 KiB load
+    static_assert(IPW >= 1, "tile too small for one load per wave");
+    static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
 };
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
@@ -77,12 +90,12 @@ __device__ __forceinline__ u32x2 tr_read(const uint8_t *p) {
     return __builtin_bit_cast(u32x2, v);
 }
 
-template <int D, bool CAUSAL, bool POS_SCALE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2, 3)))
+template <int D, int QB, int BC, int ST, bool CAUSAL, bool POS_SCALE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D * QB >= 256 ? 1 : 2, 2)))
 void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                      const uint16_t *__restrict__ V, uint16_t *__restrict__ O,
                      float *__restrict__ L, int64_t Nq, int64_t Nk, int nqt, float c) {
-    using T = Tile<D>;
+    using T = Tile<D, QB, BC, ST>;
     constexpr int S = T::STAGES;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[S * 2 * T::TILEB];
 
@@ -93,19 +106,18 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     const int64_t bh = lid / nqt;
     int qt = (int)(lid % nqt);
     if (CAUSAL) qt = nqt - 1 - qt;  // heaviest query tiles first
-    const int64_t q0 = (int64_t)qt * kBR;
-    const int64_t qw0 = q0 + wave * kQW;
-    const int64_t qrow = qw0 + lr;
+    const int64_t q0 = (int64_t)qt * T::BR;
+    const int64_t qw0 = q0 + wave * T::QW;  // query block qb of this wave: qw0 + 32qb + lane%32
     const uint16_t *Kh = K + bh * Nk * D;
     const uint16_t *Vh = V + bh * Nk * D;
 
-    int64_t nkt = (Nk + kBC - 1) / kBC;
+    int64_t nkt = (Nk + BC - 1) / BC;
     if (CAUSAL) {
-        const int64_t qlast = (q0 + kBR < Nq ? q0 + kBR : Nq) - 1;
-        const int64_t lim = qlast / kBC + 1;
+        const int64_t qlast = (q0 + T::BR < Nq ? q0 + T::BR : Nq) - 1;
+        const int64_t lim = qlast / BC + 1;
         nkt = nkt < lim ? nkt : lim;
     }
-    const int64_t qw_last = (qw0 + kQW - 1 < Nq - 1) ? qw0 + kQW - 1 : Nq - 1;
+    const int64_t qw_last = (qw0 + T::QW - 1 < Nq - 1) ? qw0 + T::QW - 1 : Nq - 1;
 
     // ---- per-lane constants of the ring loads: this lane fills LDS chunk
     //      `lane` of each of its IPW 1 KiB blocks with logical chunk
@@ -119,7 +131,7 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         ld_col[u] = ((lane % T::CH) ^ swz(row)) * 8;
     }
     auto issue = [&](int64_t j, int st) {
-        const int64_t kv0 = j * kBC;
+        const int64_t kv0 = j * BC;
         uint8_t *kb = smem + st * 2 * T::TILEB;
         uint8_t *vb = kb + T::TILEB;
 #pragma unroll
@@ -149,24 +161,31 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         voff[b] = row * T::ROWB + 16 * (chunk ^ (((s16 >> 2) << 1) | g)) + 8 * (s16 & 1);
     }
 
-    // ---- Q fragments: B operand of S^T = K Q^T (lane: query lr)
-    bf16x8 qf[D / 16];
-    {
+    // ---- Q fragments: B operands of S^T = K Q^T (lane: query lr of each block)
+    bf16x8 qf[QB][D / 16];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int64_t qrow = qw0 + 32 * qb + lr;
         const int64_t qr = qrow < Nq ? qrow : Nq - 1;
         const uint16_t *qp = Q + (bh * Nq + qr) * D + g * 8;
 #pragma unroll
         for (int ds = 0; ds < D / 16; ++ds) {
             const u32x4 w = *(const u32x4 *)(qp + ds * 16);
-            qf[ds] = __builtin_bit_cast(bf16x8, qrow < Nq ? w : u32x4{0u, 0u, 0u, 0u});
+            qf[qb][ds] = __builtin_bit_cast(bf16x8, qrow < Nq ? w : u32x4{0u, 0u, 0u, 0u});
         }
     }
 
-    f32x16 oacc[D / 32];
+    f32x16 oacc[QB][D / 32];
+    float m[QB], l[QB];
 #pragma unroll
-    for (int b = 0; b < D / 32; ++b)
+    for (int qb = 0; qb < QB; ++qb) {
+        m[qb] = -INFINITY;
+        l[qb] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
-    float m = -INFINITY, l = 0.f;
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[qb][b][r] = 0.f;
+    }
 
 #pragma unroll
     for (int t = 0; t < S - 1; ++t)
@@ -175,147 +194,176 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     for (int64_t j = 0; j < nkt; ++j) {
         // tile j has landed for this wave once only the loads issued after it
         // (tiles j+1 .. j+S-2) may still be pending
-        if (S == 3 && j + 1 < nkt)
-            wait_vm<2 * T::IPW>();
+        if (S >= 4 && j + 2 < nkt)
+            wait_vm<(S >= 4 ? 4 : 0) * T::IPW>();
+        else if (S >= 3 && j + 1 < nkt)
+            wait_vm<(S >= 3 ? 2 : 0) * T::IPW>();
         else
             wait_vm<0>();
         lds_barrier();
         if (j + S - 1 < nkt) issue(j + S - 1, (int)((j + S - 1) % S));
         const uint8_t *kbase = smem + (j % S) * 2 * T::TILEB;
         const uint8_t *vbase = kbase + T::TILEB;
-        const int64_t kv0 = j * kBC;
+        const int64_t kv0 = j * BC;
         const bool active = qw0 < Nq && (!CAUSAL || kv0 <= qw_last);
         if (!active) continue;
 
-        // ---- S^T = K_j Q^T
-        f32x16 sacc[kBC / 32];
+        // ---- S^T = K_j Q^T; each K fragment serves all QB query blocks
+        f32x16 sacc[QB][BC / 32];
 #pragma unroll
-        for (int kb = 0; kb < kBC / 32; ++kb) {
+        for (int kb = 0; kb < BC / 32; ++kb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
 #pragma unroll
             for (int ds = 0; ds < D / 16; ++ds) {
                 const bf16x8 a = *(const bf16x8 *)(kbase + kb * 32 * T::ROWB + koff[ds]);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], sacc[kb], 0, 0, 0);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    sacc[qb][kb] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ds], sacc[qb][kb], 0, 0, 0);
             }
         }
-        if (!POS_SCALE) {
+        bf16x8 pf[QB][BC / 16];
 #pragma unroll
-            for (int kb = 0; kb < kBC / 32; ++kb)
+        for (int qb = 0; qb < QB; ++qb) {
+            const int64_t qrow = qw0 + 32 * qb + lr;
+            if (!POS_SCALE) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb][r] *= c;
-        }
-        // ---- mask: keys past Nk, and keys after the query under causal.  Key
-        //      offset of register r in this lane: kb*32 + 8*(r/4) + 4g + r%4.
-        const bool need_mask = (kv0 + kBC > Nk) || (CAUSAL && kv0 + kBC - 1 > qw0);
-        if (need_mask) {
-            int64_t lim64 = Nk - 1 - kv0;  // last visible key offset
-            if (CAUSAL && qrow - kv0 < lim64) lim64 = qrow - kv0;
-            const int lim = (int)(lim64 < -1 ? -1 : (lim64 > kBC ? kBC : lim64)) - 4 * g;
+                for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < kBC / 32; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
-        }
-        // ---- online softmax (base 2).  m is a reference maximum: it is raised
-        //      (and the accumulator rescaled) only when the tile maximum exceeds it
-        //      by more than kMargin, so exponents stay <= 2^kMargin and most tiles
-        //      skip the rescale.  O = acc / l and L = m + log2 l do not depend on
-        //      which reference is used.
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < kBC / 32; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[kb][r], sacc[kb][r + 1]));
-        // this lane's half of the tile; the other half of the row is in lane ^ 32
-        const float mt = POS_SCALE ? mx * c : mx;
-        if (__any(mt > m + kMargin)) {
-            const float mj = fmaxf(mt, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                                                    xaddr, __builtin_bit_cast(int, mt))));
-            const bool grow = mj > m + kMargin;  // same in both lanes of the row
-            const float m_new = grow ? mj : m;
-            const float alpha = fast_exp2(m - m_new);  // 0 on the first tile, else <= 1
-            l *= alpha;
-#pragma unroll
-            for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
-            m = m_new;
-        }
-        const float mref = (m == -INFINITY) ? 0.f : m;
-        // ---- P^T as bf16 B operands: k-step ks uses registers 8h..8h+7 of block ks/2,
-        //      so k-slot (g, e) is key 8*(e/4) + 4g + e%4 of the step
-        bf16x8 pf[kBC / 16];
-        float lsum = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < kBC / 16; ++ks) {
-            const int kb = ks >> 1, h = ks & 1;
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                p[e] = fast_exp2(POS_SCALE ? fmaf(sacc[kb][8 * h + e], c, -mref)
-                                           : sacc[kb][8 * h + e] - mref);
-                lsum += p[e];
+                    for (int r = 0; r < 16; ++r) sacc[qb][kb][r] *= c;
             }
-            const u32x4 w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                             pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-            pf[ks] = __builtin_bit_cast(bf16x8, w);
-        }
-        l += lsum;  // this lane's half of the tile's keys
-        // ---- O^T += V_j^T P^T; V^T read transposed in the same k-slot order
+            // ---- mask: keys past Nk, and keys after the query under causal.  Key
+            //      offset of register r in this lane: kb*32 + 8*(r/4) + 4g + r%4.
+            const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > qw0 + 32 * qb);
+            if (need_mask) {
+                int64_t lim64 = Nk - 1 - kv0;  // last visible key offset
+                if (CAUSAL && qrow - kv0 < lim64) lim64 = qrow - kv0;
+                const int lim = (int)(lim64 < -1 ? -1 : (lim64 > BC ? BC : lim64)) - 4 * g;
 #pragma unroll
-        for (int ks = 0; ks < kBC / 16; ++ks) {
+                for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[qb][kb][r] = -INFINITY;
+            }
+            // ---- online softmax (base 2).  m is a reference maximum: it is raised
+            //      (and the accumulator rescaled) only when the tile maximum exceeds
+            //      it by more than kMargin, so exponents stay <= 2^kMargin and most
+            //      tiles skip the rescale.  O = acc / l and L = m + log2 l do not
+            //      depend on which reference is used.
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2)
+                    mx = fmaxf(mx, fmaxf(sacc[qb][kb][r], sacc[qb][kb][r + 1]));
+            // this lane's half of the tile; the other half of the row is in lane ^ 32
+            const float mt = POS_SCALE ? mx * c : mx;
+            if (__any(mt > m[qb] + kMargin)) {
+                const float mj = fmaxf(mt, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                                        xaddr, __builtin_bit_cast(int, mt))));
+                const bool grow = mj > m[qb] + kMargin;  // same in both lanes of the row
+                const float m_new = grow ? mj : m[qb];
+                const float alpha = fast_exp2(m[qb] - m_new);  // 0 on the first tile, else <= 1
+                l[qb] *= alpha;
+#pragma unroll
+                for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[qb][b][r] *= alpha;
+                m[qb] = m_new;
+            }
+            const float mref = (m[qb] == -INFINITY) ? 0.f : m[qb];
+            // ---- P^T as bf16 B operands: k-step ks uses registers 8h..8h+7 of block
+            //      ks/2, so k-slot (g, e) is key 8*(e/4) + 4g + e%4 of the step
+            float lsum = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < BC / 16; ++ks) {
+                const int kb = ks >> 1, h = ks & 1;
+                float p[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    p[e] = fast_exp2(POS_SCALE ? fmaf(sacc[qb][kb][8 * h + e], c, -mref)
+                                               : sacc[qb][kb][8 * h + e] - mref);
+                    lsum += p[e];
+                }
+                const u32x4 w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+                pf[qb][ks] = __builtin_bit_cast(bf16x8, w);
+            }
+            l[qb] += lsum;  // this lane's half of the tile's keys
+        }
+        // ---- O^T += V_j^T P^T; V^T read transposed in the same k-slot order and
+        //      shared by the QB query blocks
+#pragma unroll
+        for (int ks = 0; ks < BC / 16; ++ks) {
 #pragma unroll
             for (int b = 0; b < D / 32; ++b) {
                 const uint8_t *p = vbase + voff[b] + ks * 16 * T::ROWB;
                 const u32x2 lo = tr_read(p), hi = tr_read(p + 8 * T::ROWB);
                 const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-                oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, w), pf[ks], oacc[b], 0, 0, 0);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    oacc[qb][b] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][ks], oacc[qb][b], 0, 0, 0);
             }
         }
     }
 
     // ---- epilogue: one division, natural-log L
-    const float l_tot = l + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                    xaddr, __builtin_bit_cast(int, l)));
-    if (qrow < Nq) {
-        const float inv = 1.f / l_tot;
-        uint16_t *orow = O + (bh * Nq + qrow) * D;
 #pragma unroll
-        for (int b = 0; b < D / 32; ++b)
+    for (int qb = 0; qb < QB; ++qb) {
+        const int64_t qrow = qw0 + 32 * qb + lr;
+        const float l_tot = l[qb] + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                            xaddr, __builtin_bit_cast(int, l[qb])));
+        if (qrow < Nq) {
+            const float inv = 1.f / l_tot;
+            uint16_t *orow = O + (bh * Nq + qrow) * D;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const u32x2 w = {pack_bf16x2(oacc[b][4 * t] * inv, oacc[b][4 * t + 1] * inv),
-                                 pack_bf16x2(oacc[b][4 * t + 2] * inv, oacc[b][4 * t + 3] * inv)};
-                *(u32x2 *)(orow + b * 32 + 8 * t + 4 * g) = w;
-            }
-        if (g == 0) L[bh * Nq + qrow] = (m + log2f(l_tot)) * kLn2;
+            for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const u32x2 w = {
+                        pack_bf16x2(oacc[qb][b][4 * t] * inv, oacc[qb][b][4 * t + 1] * inv),
+                        pack_bf16x2(oacc[qb][b][4 * t + 2] * inv, oacc[qb][b][4 * t + 3] * inv)};
+                    *(u32x2 *)(orow + b * 32 + 8 * t + 4 * g) = w;
+                }
+            if (g == 0) L[bh * Nq + qrow] = (m[qb] + log2f(l_tot)) * kLn2;
+        }
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, int QB, int BC, int ST, bool CAUSAL>
 hipError_t launch_d(const FwdArgs &a, hipStream_t s) {
-    const int nqt = (int)((a.Nq + kBR - 1) / kBR);
+    using T = Tile<D, QB, BC, ST>;
+    const int nqt = (int)((a.Nq + T::BR - 1) / T::BR);
     const dim3 grid((unsigned)(a.B * a.H * nqt));
     const float c = a.scale * kLog2e;
     if (a.scale > 0.f)
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true>), grid, dim3(kThreads), 0, s,
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BC, ST, CAUSAL, true>), grid, dim3(kThreads), 0, s,
                            (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
                            (uint16_t *)a.O, a.L, a.Nq, a.Nk, nqt, c);
     else
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false>), grid, dim3(kThreads), 0, s,
-                           (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BC, ST, CAUSAL, false>), grid, dim3(kThreads), 0,
+                           s, (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
                            (uint16_t *)a.O, a.L, a.Nq, a.Nk, nqt, c);
     return hipGetLastError();
 }
 
+// Tile configurations (chosen by measurement on MI355X).
+constexpr int kQB64 = FA_FWD_QB64, kBC64 = FA_FWD_BC64, kST64 = FA_FWD_ST64;
+constexpr int kQB128 = FA_FWD_QB128, kBC128 = FA_FWD_BC128, kST128 = FA_FWD_ST128;
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s) {
-    if (a.d == 128) return a.causal ? launch_d<128, true>(a, s) : launch_d<128, false>(a, s);
-    return a.causal ? launch_d<64, true>(a, s) : launch_d<64, false>(a, s);
+    if (a.d == 128)
+        return a.causal ? launch_d<128, kQB128, kBC128, kST128, true>(a, s)
+                        : launch_d<128, kQB128, kBC128, kST128, false>(a, s);
+    return a.causal ? launch_d<64, kQB64, kBC64, kST64, true>(a, s)
+                    : launch_d<64, kQB64, kBC64, kST64, false>(a, s);
 }
 
 }  // namespace fa
