@@ -12,53 +12,42 @@
 // recomputing two of the five products.  The result is also deterministic.
 //
 // Three launches on the caller's stream:
-//   bwd_pre_kernel   D = rowsum(dO * O) in fp32;
+//   bwd_pre_kernel   D = rowsum(dO * O) and L2 = L * log2(e), fp32;
 //   bwd_dkdv_kernel  one workgroup per (batch*head, 128-key tile), 4 waves of 32
-//                    keys, K and V in registers; walks the query tiles that can
-//                    see its keys; writes dK, dV;
+//                    keys, K and V in registers; Q, dO, L2 and D tiles of the
+//                    query tiles that can see its keys stream through an LDS ring;
 //   bwd_dq_kernel    one workgroup per (batch*head, 128-query tile), 4 waves of
-//                    32 queries, Q and dO in registers; walks the key tiles its
-//                    queries can see; writes dQ.
+//                    32 queries, Q and dO in registers; K and V tiles of the key
+//                    tiles its queries can see stream through an LDS ring.
+// Both rings are filled with global_load_lds_dwordx4 into row-major,
+// chunk-swizzled tiles (see fa_device.h), one barrier per tile.
 //
 // Layouts (v_mfma_f32_32x32x16_bf16, C[m][n] with lane = n):
 //   dkdv: S = Q K^T and dP = dO V^T put one KEY per lane, so P and dS are
-//         directly the B operands of dV^T = dO^T P and dK^T = Q^T dS.
+//         directly the B operands of dV^T = dO^T P and dK^T = Q^T dS, with dO^T
+//         and Q^T read transposed from the row-major tiles.
 //   dq:   S^T = K Q^T and dP^T = V dO^T put one QUERY per lane, so dS^T is
-//         directly the B operand of dQ^T = K^T dS^T, and L, D are per-lane.
-//   The transposed operands (dO^T, Q^T, K^T) are read from row-major LDS tiles
-//   with ds_read_b64_tr_b16: within each 16-lane group, lane i receives
-//   element i%4 of the 8-byte pieces addressed by lanes i/4 + 4t (t = 0..3),
-//   so lanes that address a 4-row x 16-column block receive its columns.
+//         directly the B operand of dQ^T = K^T dS^T (K^T read transposed), and
+//         L2, D are per-lane scalars.
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-
-// Transposed read of a 4-row x 16-column block of a row-major bf16 LDS tile
-// whose top-left element is `base`: lane i of each 16-lane group receives the
-// 4 elements of column i.  `s` is the lane's index within its group.
-__device__ __forceinline__ u32x2 tr_read(const uint16_t *base, int stride, int s) {
-    const uint16_t *p = base + (s >> 2) * stride + 4 * (s & 3);
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4 *)(p));
-    return __builtin_bit_cast(u32x2, v);
-}
-
-__device__ __forceinline__ bf16x8 join(u32x2 a, u32x2 b) {
-    const u32x4 w = {a[0], a[1], b[0], b[1]};
-    return __builtin_bit_cast(bf16x8, w);
-}
 
 // Eight fp32 accumulator registers r0..r0+7 -> bf16x8 (round to nearest even).
 __device__ __forceinline__ bf16x8 pack8(const f32x16 &v, int r0) {
     const u32x4 w = {pack_bf16x2(v[r0 + 0], v[r0 + 1]), pack_bf16x2(v[r0 + 2], v[r0 + 3]),
                      pack_bf16x2(v[r0 + 4], v[r0 + 5]), pack_bf16x2(v[r0 + 6], v[r0 + 7])};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ bf16x8 tr_pair(const uint8_t *p, int row_bytes8) {
+    const u32x2 lo = tr_read(p), hi = tr_read(p + row_bytes8);
+    const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
     return __builtin_bit_cast(bf16x8, w);
 }
 
@@ -72,12 +61,14 @@ __device__ __forceinline__ u32x4 load_row16(const uint16_t *base, int64_t row, i
 }
 
 // ---------------------------------------------------------------------------
-// D = rowsum(dO * O) (fp32).
+// D = rowsum(dO * O) and L2 = L * log2(e) (fp32).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict__ O,
                                                       const uint16_t *__restrict__ dO,
-                                                      float *__restrict__ Dv, int64_t rows) {
+                                                      const float *__restrict__ L,
+                                                      float *__restrict__ Dv,
+                                                      float *__restrict__ L2, int64_t rows) {
     constexpr int LPR = D / 8;  // lanes per row (16-byte chunks)
     const int64_t chunk = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t row = chunk / LPR;
@@ -95,37 +86,57 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
     // sum over the LPR lanes of the row (aligned groups of 8 or 16 lanes)
 #pragma unroll
     for (int o = 1; o < LPR; o <<= 1) s += __shfl_xor(s, o);
-    if (row < rows && sub == 0) Dv[row] = s;
+    if (row < rows && sub == 0) {
+        Dv[row] = s;
+        L2[row] = L[row] * kLog2e;
+    }
+}
+
+// Per-lane LDS offsets shared by both kernels, for a tile of ROWB-byte rows:
+//   row_off(ds): 16-byte operand of row (lane%32), logical chunk 2*ds + g;
+//   tr_off(b):   transposed read at rows 4g + lane%16/4 (+16k, +8), columns
+//                32b + 16*((lane/16)%2) + 4*(lane%4).
+__device__ __forceinline__ int row_off(int lr, int g, int ds, int ROWB) {
+    return lr * ROWB + 16 * ((2 * ds + g) ^ swz(lr));
+}
+__device__ __forceinline__ int tr_off(int lane, int b, int ROWB) {
+    const int g = lane >> 5, s = lane & 15, G = lane >> 4;
+    const int row = 4 * g + (s >> 2);
+    const int chunk = 4 * b + 2 * (G & 1) + ((s >> 1) & 1);
+    return row * ROWB + 16 * (chunk ^ (((s >> 2) << 1) | g)) + 8 * (s & 1);
 }
 
 // ---------------------------------------------------------------------------
 // dK, dV: key-major.
 // ---------------------------------------------------------------------------
-template <int D>
-struct DkdvTile {
-    static constexpr int KEYS = 32 * kWaves;    // keys per workgroup
-    static constexpr int QB = D == 64 ? 2 : 1;  // 32-query blocks per query tile
-    static constexpr int BR = 32 * QB;          // queries per query tile
-    static constexpr int RS = D + 8;            // LDS row stride (elements)
-    static constexpr int QCH = BR * D / 8 / kThreads;  // 16-byte chunks per thread per tensor
+template <int D, int BR_, int ST_>
+struct DkdvCfg {
+    static constexpr int BR = BR_;                 // queries per tile
+    static constexpr int QB = BR / 32;             // 32-query blocks per tile
+    static constexpr int KEYS = 32 * kWaves;       // keys per workgroup
+    static constexpr int CH = D / 8, ROWB = D * 2;
+    static constexpr int TILEB = BR * ROWB;        // one Q or dO tile
+    static constexpr int VECB = 256;               // one L2 or D slice (64 lanes x 4 B)
+    static constexpr int STAGEB = 2 * TILEB + 2 * VECB;
+    static constexpr int ST = ST_;
+    static constexpr int IPW = TILEB / 1024 / kWaves;
+    static constexpr int RPI = 1024 / ROWB;
+    static_assert(IPW >= 1 && BR <= 64 && ST >= 2 && ST <= 3, "dkdv tile");
 };
 
-template <int D, bool CAUSAL>
+template <int D, int BR, int ST, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, 2)))
 void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                      const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
-                     const float *__restrict__ L, const float *__restrict__ Dv,
+                     const float *__restrict__ L2, const float *__restrict__ Dv,
                      uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int64_t Nq, int64_t Nk,
                      int nkt, float scale, float c) {
-    using T = DkdvTile<D>;
-    constexpr int QB = T::QB, BR = T::BR, RS = T::RS;
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BR * RS];
-    __shared__ __attribute__((aligned(16))) uint16_t sdO[2][BR * RS];
-    __shared__ __attribute__((aligned(16))) float sL[2][BR];
-    __shared__ __attribute__((aligned(16))) float sD[2][BR];
+    using T = DkdvCfg<D, BR, ST>;
+    constexpr int QB = T::QB, ROWB = T::ROWB;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * T::STAGEB];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int g = lane >> 5, lr = lane & 31, s16 = lane & 15, G = lane >> 4;
+    const int g = lane >> 5, lr = lane & 31;
     const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = lid / nkt;
     const int kt = (int)(lid % nkt);  // causal: low key tiles see the most queries; go first
@@ -134,18 +145,50 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     const int64_t mykey = kw0 + lr;
     const uint16_t *Qh = Q + bh * Nq * D;
     const uint16_t *dOh = dO + bh * Nq * D;
-    const uint16_t *Kh = K + bh * Nk * D;
-    const uint16_t *Vh = V + bh * Nk * D;
-    const float *Lh = L + bh * Nq;
+    const float *L2h = L2 + bh * Nq;
     const float *Dh = Dv + bh * Nq;
 
     // K and V of this wave's keys: B operands of S = Q K^T and dP = dO V^T
     bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) {
-        kf[ds] = __builtin_bit_cast(bf16x8, load_row16(Kh, mykey, Nk, D, ds * 2 + g));
-        vf[ds] = __builtin_bit_cast(bf16x8, load_row16(Vh, mykey, Nk, D, ds * 2 + g));
+        kf[ds] = __builtin_bit_cast(bf16x8, load_row16(K + bh * Nk * D, mykey, Nk, D, ds * 2 + g));
+        vf[ds] = __builtin_bit_cast(bf16x8, load_row16(V + bh * Nk * D, mykey, Nk, D, ds * 2 + g));
     }
+
+    // ring loads: this lane fills chunk `lane` of its IPW 1 KiB blocks of the
+    // Q and dO tiles; waves 0 and 1 also fill the L2 and D slices
+    int ld_row[T::IPW], ld_col[T::IPW];
+#pragma unroll
+    for (int u = 0; u < T::IPW; ++u) {
+        const int row = (wave * T::IPW + u) * T::RPI + lane / T::CH;
+        ld_row[u] = row;
+        ld_col[u] = ((lane % T::CH) ^ swz(row)) * 8;
+    }
+    auto issue = [&](int it, int st) {
+        const int64_t q0 = (int64_t)it * BR;
+        uint8_t *qb = smem + st * T::STAGEB;
+        uint8_t *ob = qb + T::TILEB;
+#pragma unroll
+        for (int u = 0; u < T::IPW; ++u) {
+            int64_t q = q0 + ld_row[u];
+            q = q < Nq ? q : Nq - 1;  // past the end: a real row, masked in compute
+            const int blk = wave * T::IPW + u;
+            dma16(Qh + q * D + ld_col[u], qb + blk * 1024);
+            dma16(dOh + q * D + ld_col[u], ob + blk * 1024);
+        }
+        if (wave < 2) {
+            int64_t q = q0 + lane;
+            q = q < Nq ? q : Nq - 1;
+            dma4((wave == 0 ? L2h : Dh) + q, ob + T::TILEB + wave * T::VECB);
+        }
+    };
+
+    int qoff[D / 16], toff[D / 32];
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) qoff[ds] = row_off(lr, g, ds, ROWB);
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) toff[b] = tr_off(lane, b, ROWB);
 
     f32x16 dvacc[D / 32], dkacc[D / 32];
 #pragma unroll
@@ -159,116 +202,90 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     // query tiles that can see this key tile
     const int nqt = (int)((Nq + BR - 1) / BR);
     const int it0 = CAUSAL ? (int)(k0 / BR) : 0;
-
-    u32x4 qreg[T::QCH], oreg[T::QCH];
-    float lreg = 0.f, dreg = 0.f;
-    auto load_q = [&](int it) {
-        const int64_t q0 = (int64_t)it * BR;
 #pragma unroll
-        for (int u = 0; u < T::QCH; ++u) {
-            const int cidx = tid + kThreads * u;
-            const int row = cidx / (D / 8), col = cidx % (D / 8);
-            qreg[u] = load_row16(Qh, q0 + row, Nq, D, col);
-            oreg[u] = load_row16(dOh, q0 + row, Nq, D, col);
-        }
-        if (tid < BR) {
-            const int64_t q = q0 + tid;
-            const int64_t qc = q < Nq ? q : Nq - 1;
-            // a padded query row gets L = +inf, so its P is exactly 0
-            lreg = q < Nq ? Lh[qc] * kLog2e : INFINITY;
-            dreg = q < Nq ? Dh[qc] : 0.f;
-        }
-    };
-    auto store_q = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < T::QCH; ++u) {
-            const int cidx = tid + kThreads * u;
-            const int row = cidx / (D / 8), col = cidx % (D / 8);
-            *(u32x4 *)(&sQ[buf][row * RS + col * 8]) = qreg[u];
-            *(u32x4 *)(&sdO[buf][row * RS + col * 8]) = oreg[u];
-        }
-        if (tid < BR) {
-            sL[buf][tid] = lreg;
-            sD[buf][tid] = dreg;
-        }
-    };
-
-    if (it0 < nqt) {
-        load_q(it0);
-        store_q(0);
-    }
-    __syncthreads();
+    for (int t = 0; t < ST - 1; ++t)
+        if (it0 + t < nqt) issue(it0 + t, t);
 
     for (int it = it0; it < nqt; ++it) {
-        const int buf = (it - it0) & 1;
+        const int idx = it - it0;
+        if (ST == 3 && it + 1 < nqt) {
+            if (wave < 2)
+                wait_vm<(ST == 3 ? 2 * T::IPW + 1 : 0)>();
+            else
+                wait_vm<(ST == 3 ? 2 * T::IPW : 0)>();
+        } else {
+            wait_vm<0>();
+        }
+        lds_barrier();
+        if (it + ST - 1 < nqt) issue(it + ST - 1, (idx + ST - 1) % ST);
         const int64_t q0 = (int64_t)it * BR;
-        if (it + 1 < nqt) load_q(it + 1);
         const bool active = kw0 < Nk && (!CAUSAL || q0 + BR - 1 >= kw0);
-        if (active) {
-            // ---- S = Q K^T and dP = dO V^T (lane: key lr; register r: query
-            //      8*(r/4) + 4g + r%4 of the 32-query block)
-            f32x16 sacc[QB], pacc[QB];
+        if (!active) continue;
+        const uint8_t *qt = smem + (idx % ST) * T::STAGEB;
+        const uint8_t *ot = qt + T::TILEB;
+        const float *lt = (const float *)(ot + T::TILEB);
+        const float *dt = lt + T::VECB / 4;
+
+        // ---- S = Q K^T and dP = dO V^T (lane: key lr; register r: query
+        //      8*(r/4) + 4g + r%4 of the 32-query block)
+        f32x16 sacc[QB], pacc[QB];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    sacc[qb][r] = 0.f;
-                    pacc[qb][r] = 0.f;
-                }
-#pragma unroll
-                for (int ds = 0; ds < D / 16; ++ds) {
-                    const int off = (qb * 32 + lr) * RS + ds * 16 + g * 8;
-                    const bf16x8 aq = *(const bf16x8 *)(&sQ[buf][off]);
-                    const bf16x8 ao = *(const bf16x8 *)(&sdO[buf][off]);
-                    sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ds], sacc[qb], 0, 0,
-                                                                       0);
-                    pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[ds], pacc[qb], 0, 0,
-                                                                       0);
-                }
+            for (int r = 0; r < 16; ++r) {
+                sacc[qb][r] = 0.f;
+                pacc[qb][r] = 0.f;
             }
-            // ---- P = exp2(S c - L log2 e), dS = P (dP - D)
-            const bool need_mask = (kw0 + 32 > Nk) || (CAUSAL && q0 < kw0 + 31);
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
+            for (int ds = 0; ds < D / 16; ++ds) {
+                const int off = qb * 32 * ROWB + qoff[ds];
+                const bf16x8 aq = *(const bf16x8 *)(qt + off);
+                const bf16x8 ao = *(const bf16x8 *)(ot + off);
+                sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ds], sacc[qb], 0, 0, 0);
+                pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[ds], pacc[qb], 0, 0, 0);
+            }
+        }
+        // ---- P = exp2(S c - L2), dS = P (dP - D); zero past Nq, past Nk, and
+        //      (causal) where the key comes after the query
+        const bool need_mask =
+            (q0 + BR > Nq) || (kw0 + 32 > Nk) || (CAUSAL && q0 < kw0 + 31);
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int qi = qb * 32 + 8 * r4 + 4 * g;
-                    const f32x4 lv = *(const f32x4 *)(&sL[buf][qi]);
-                    const f32x4 dv = *(const f32x4 *)(&sD[buf][qi]);
+        for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * r4 + e;
-                        float p = fast_exp2(fmaf(sacc[qb][r], c, -lv[e]));
-                        if (need_mask && (mykey >= Nk || (CAUSAL && mykey > q0 + qi + e)))
-                            p = 0.f;
-                        sacc[qb][r] = p;
-                        pacc[qb][r] = p * (pacc[qb][r] - dv[e]);
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int qi = qb * 32 + 8 * r4 + 4 * g;
+                const f32x4 lv = *(const f32x4 *)(lt + qi);
+                const f32x4 dv = *(const f32x4 *)(dt + qi);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * r4 + e;
+                    float p = fast_exp2(fmaf(sacc[qb][r], c, -lv[e]));
+                    if (need_mask) {
+                        const int64_t q = q0 + qi + e;
+                        if (q >= Nq || mykey >= Nk || (CAUSAL && mykey > q)) p = 0.f;
                     }
-                }
-            }
-            // ---- dV^T += dO^T P and dK^T += Q^T dS.  B operand (k-step kq of 16
-            //      queries) = registers 8h..8h+7 of block kq/2, so k-slot (g, e) is
-            //      query 8*(e/4) + 4g + e%4 of the step; the A operand (lane: column
-            //      32b + lane%32) is read transposed with the same slot order.
-#pragma unroll
-            for (int kq = 0; kq < BR / 16; ++kq) {
-                const bf16x8 pb = pack8(sacc[kq >> 1], 8 * (kq & 1));
-                const bf16x8 sb = pack8(pacc[kq >> 1], 8 * (kq & 1));
-                const int r0 = kq * 16 + 4 * g;
-#pragma unroll
-                for (int b = 0; b < D / 32; ++b) {
-                    const int col = b * 32 + 16 * (G & 1);
-                    const bf16x8 ao = join(tr_read(&sdO[buf][r0 * RS + col], RS, s16),
-                                           tr_read(&sdO[buf][(r0 + 8) * RS + col], RS, s16));
-                    const bf16x8 aq = join(tr_read(&sQ[buf][r0 * RS + col], RS, s16),
-                                           tr_read(&sQ[buf][(r0 + 8) * RS + col], RS, s16));
-                    dvacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb, dvacc[b], 0, 0, 0);
-                    dkacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb, dkacc[b], 0, 0, 0);
+                    sacc[qb][r] = p;
+                    pacc[qb][r] = p * (pacc[qb][r] - dv[e]);
                 }
             }
         }
-        if (it + 1 < nqt) store_q(buf ^ 1);
-        __syncthreads();
+        // ---- dV^T += dO^T P and dK^T += Q^T dS.  B operand (k-step kq of 16
+        //      queries) = registers 8h..8h+7 of block kq/2, so k-slot (g, e) is
+        //      query 8*(e/4) + 4g + e%4 of the step; the transposed A operand is
+        //      read in the same slot order.
+#pragma unroll
+        for (int kq = 0; kq < BR / 16; ++kq) {
+            const bf16x8 pb = pack8(sacc[kq >> 1], 8 * (kq & 1));
+            const bf16x8 sb = pack8(pacc[kq >> 1], 8 * (kq & 1));
+#pragma unroll
+            for (int b = 0; b < D / 32; ++b) {
+                const int off = toff[b] + kq * 16 * ROWB;
+                const bf16x8 ao = tr_pair(ot + off, 8 * ROWB);
+                const bf16x8 aq = tr_pair(qt + off, 8 * ROWB);
+                dvacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb, dvacc[b], 0, 0, 0);
+                dkacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb, dkacc[b], 0, 0, 0);
+            }
+        }
     }
 
     // ---- epilogue: dK = scale * dK_acc, dV = dV_acc (lane: key lr; register r:
@@ -295,37 +312,45 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
 // ---------------------------------------------------------------------------
 // dQ: query-major.
 // ---------------------------------------------------------------------------
-constexpr int kDqBR = 32 * kWaves;  // queries per workgroup
-constexpr int kDqBC = 64;           // keys per tile
+template <int D, int BC_, int ST_>
+struct DqCfg {
+    static constexpr int BR = 32 * kWaves;          // queries per workgroup
+    static constexpr int BC = BC_;                  // keys per tile
+    static constexpr int CH = D / 8, ROWB = D * 2;
+    static constexpr int TILEB = BC * ROWB;
+    static constexpr int ST = ST_;
+    static constexpr int IPW = TILEB / 1024 / kWaves;
+    static constexpr int RPI = 1024 / ROWB;
+    static_assert(IPW >= 1 && ST >= 2 && ST <= 3, "dq tile");
+};
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, 2)))
+template <int D, int BC, int ST, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                    const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
-                   const float *__restrict__ L, const float *__restrict__ Dv,
+                   const float *__restrict__ L2, const float *__restrict__ Dv,
                    uint16_t *__restrict__ dQ, int64_t Nq, int64_t Nk, int nqt, float scale,
                    float c) {
-    constexpr int RS = D + 8;
-    constexpr int KCH = kDqBC * D / 8 / kThreads;  // 16-byte chunks per thread per tensor
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kDqBC * RS];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][kDqBC * RS];
+    using T = DqCfg<D, BC, ST>;
+    constexpr int ROWB = T::ROWB;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * 2 * T::TILEB];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int g = lane >> 5, lr = lane & 31, s16 = lane & 15, G = lane >> 4;
+    const int g = lane >> 5, lr = lane & 31;
     const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = lid / nqt;
     int qt = (int)(lid % nqt);
     if (CAUSAL) qt = nqt - 1 - qt;  // heaviest query tiles first
-    const int64_t q0 = (int64_t)qt * kDqBR;
+    const int64_t q0 = (int64_t)qt * T::BR;
     const int64_t qw0 = q0 + wave * 32;
     const int64_t qrow = qw0 + lr;
     const uint16_t *Kh = K + bh * Nk * D;
     const uint16_t *Vh = V + bh * Nk * D;
 
-    int64_t nkt = (Nk + kDqBC - 1) / kDqBC;
+    int64_t nkt = (Nk + BC - 1) / BC;
     if (CAUSAL) {
-        const int64_t qlast = (q0 + kDqBR < Nq ? q0 + kDqBR : Nq) - 1;
-        const int64_t lim = qlast / kDqBC + 1;
+        const int64_t qlast = (q0 + T::BR < Nq ? q0 + T::BR : Nq) - 1;
+        const int64_t lim = qlast / BC + 1;
         nkt = nkt < lim ? nkt : lim;
     }
     const int64_t qw_last = (qw0 + 31 < Nq - 1) ? qw0 + 31 : Nq - 1;
@@ -338,8 +363,34 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
         of[ds] = __builtin_bit_cast(bf16x8, load_row16(dO + bh * Nq * D, qrow, Nq, D, ds * 2 + g));
     }
     const int64_t qc = qrow < Nq ? qrow : Nq - 1;
-    const float l2 = qrow < Nq ? L[bh * Nq + qc] * kLog2e : INFINITY;  // padded row: P = 0
+    const float l2 = qrow < Nq ? L2[bh * Nq + qc] : INFINITY;  // padded row: P = 0
     const float dq = qrow < Nq ? Dv[bh * Nq + qc] : 0.f;
+
+    int ld_row[T::IPW], ld_col[T::IPW];
+#pragma unroll
+    for (int u = 0; u < T::IPW; ++u) {
+        const int row = (wave * T::IPW + u) * T::RPI + lane / T::CH;
+        ld_row[u] = row;
+        ld_col[u] = ((lane % T::CH) ^ swz(row)) * 8;
+    }
+    auto issue = [&](int64_t j, int st) {
+        const int64_t kv0 = j * BC;
+        uint8_t *kb = smem + st * 2 * T::TILEB;
+        uint8_t *vb = kb + T::TILEB;
+#pragma unroll
+        for (int u = 0; u < T::IPW; ++u) {
+            int64_t key = kv0 + ld_row[u];
+            key = key < Nk ? key : Nk - 1;  // past the end: a real row, masked later
+            const int blk = wave * T::IPW + u;
+            dma16(Kh + key * D + ld_col[u], kb + blk * 1024);
+            dma16(Vh + key * D + ld_col[u], vb + blk * 1024);
+        }
+    };
+    int koff[D / 16], toff[D / 32];
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) koff[ds] = row_off(lr, g, ds, ROWB);
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) toff[b] = tr_off(lane, b, ROWB);
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -347,90 +398,70 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
 
-    u32x4 kreg[KCH], vreg[KCH];
-    auto load_kv = [&](int64_t j) {
-        const int64_t kv0 = j * kDqBC;
 #pragma unroll
-        for (int u = 0; u < KCH; ++u) {
-            const int cidx = tid + kThreads * u;
-            const int row = cidx / (D / 8), col = cidx % (D / 8);
-            kreg[u] = load_row16(Kh, kv0 + row, Nk, D, col);
-            vreg[u] = load_row16(Vh, kv0 + row, Nk, D, col);
-        }
-    };
-    auto store_kv = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < KCH; ++u) {
-            const int cidx = tid + kThreads * u;
-            const int row = cidx / (D / 8), col = cidx % (D / 8);
-            *(u32x4 *)(&sK[buf][row * RS + col * 8]) = kreg[u];
-            *(u32x4 *)(&sV[buf][row * RS + col * 8]) = vreg[u];
-        }
-    };
-
-    load_kv(0);
-    store_kv(0);
-    __syncthreads();
+    for (int t = 0; t < ST - 1; ++t)
+        if (t < nkt) issue(t, t);
 
     for (int64_t j = 0; j < nkt; ++j) {
-        const int buf = (int)(j & 1);
-        if (j + 1 < nkt) load_kv(j + 1);
-        const int64_t kv0 = j * kDqBC;
+        if (ST == 3 && j + 1 < nkt)
+            wait_vm<(ST == 3 ? 2 * T::IPW : 0)>();
+        else
+            wait_vm<0>();
+        lds_barrier();
+        if (j + ST - 1 < nkt) issue(j + ST - 1, (int)((j + ST - 1) % ST));
+        const int64_t kv0 = j * BC;
         const bool active = qw0 < Nq && (!CAUSAL || kv0 <= qw_last);
-        if (active) {
-            // ---- S^T = K Q^T, dP^T = V dO^T (lane: query lr; register r: key
-            //      8*(r/4) + 4g + r%4 of the 32-key block)
-            f32x16 sacc[kDqBC / 32], pacc[kDqBC / 32];
+        if (!active) continue;
+        const uint8_t *kt = smem + (j % ST) * 2 * T::TILEB;
+        const uint8_t *vt = kt + T::TILEB;
+
+        // ---- S^T = K Q^T, dP^T = V dO^T (lane: query lr; register r: key
+        //      8*(r/4) + 4g + r%4 of the 32-key block)
+        f32x16 sacc[BC / 32], pacc[BC / 32];
 #pragma unroll
-            for (int kb = 0; kb < kDqBC / 32; ++kb) {
+        for (int kb = 0; kb < BC / 32; ++kb) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    sacc[kb][r] = 0.f;
-                    pacc[kb][r] = 0.f;
-                }
-#pragma unroll
-                for (int ds = 0; ds < D / 16; ++ds) {
-                    const int off = (kb * 32 + lr) * RS + ds * 16 + g * 8;
-                    const bf16x8 ak = *(const bf16x8 *)(&sK[buf][off]);
-                    const bf16x8 av = *(const bf16x8 *)(&sV[buf][off]);
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[ds], sacc[kb], 0, 0,
-                                                                       0);
-                    pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[ds], pacc[kb], 0, 0,
-                                                                       0);
-                }
+            for (int r = 0; r < 16; ++r) {
+                sacc[kb][r] = 0.f;
+                pacc[kb][r] = 0.f;
             }
-            // ---- P = exp2(S c - L log2 e), dS = P (dP - D), both per lane
-            const bool need_mask = (kv0 + kDqBC > Nk) || (CAUSAL && kv0 + kDqBC - 1 > qw0);
 #pragma unroll
-            for (int kb = 0; kb < kDqBC / 32; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(fmaf(sacc[kb][r], c, -l2));
-                    if (need_mask) {
-                        const int64_t key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                        if (key >= Nk || (CAUSAL && key > qrow)) p = 0.f;
-                    }
-                    pacc[kb][r] = p * (pacc[kb][r] - dq);
-                }
-            // ---- dQ^T += K^T dS^T.  B operand (k-step ks of 16 keys) = registers
-            //      8h..8h+7 of block ks/2: k-slot (g, e) is key 8*(e/4) + 4g + e%4 of
-            //      the step; K^T (lane: column 32b + lane%32) is read transposed in
-            //      the same slot order.
-#pragma unroll
-            for (int ks = 0; ks < kDqBC / 16; ++ks) {
-                const bf16x8 sb = pack8(pacc[ks >> 1], 8 * (ks & 1));
-                const int r0 = ks * 16 + 4 * g;
-#pragma unroll
-                for (int b = 0; b < D / 32; ++b) {
-                    const int col = b * 32 + 16 * (G & 1);
-                    const bf16x8 a = join(tr_read(&sK[buf][r0 * RS + col], RS, s16),
-                                          tr_read(&sK[buf][(r0 + 8) * RS + col], RS, s16));
-                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, acc[b], 0, 0, 0);
-                }
+            for (int ds = 0; ds < D / 16; ++ds) {
+                const int off = kb * 32 * ROWB + koff[ds];
+                const bf16x8 ak = *(const bf16x8 *)(kt + off);
+                const bf16x8 av = *(const bf16x8 *)(vt + off);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[ds], sacc[kb], 0, 0, 0);
+                pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[ds], pacc[kb], 0, 0, 0);
             }
         }
-        if (j + 1 < nkt) store_kv(buf ^ 1);
-        __syncthreads();
+        // ---- P = exp2(S c - L2), dS = P (dP - D), both per lane
+        const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > qw0);
+        int lim = BC;
+        if (need_mask) {
+            int64_t lim64 = Nk - 1 - kv0;  // last visible key offset
+            if (CAUSAL && qrow - kv0 < lim64) lim64 = qrow - kv0;
+            lim = (int)(lim64 < -1 ? -1 : (lim64 > BC ? BC : lim64)) - 4 * g;
+        }
+#pragma unroll
+        for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float p = fast_exp2(fmaf(sacc[kb][r], c, -l2));
+                if (need_mask && kb * 32 + 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
+                pacc[kb][r] = p * (pacc[kb][r] - dq);
+            }
+        // ---- dQ^T += K^T dS^T.  B operand (k-step ks of 16 keys) = registers
+        //      8h..8h+7 of block ks/2: k-slot (g, e) is key 8*(e/4) + 4g + e%4 of
+        //      the step; K^T is read transposed in the same slot order.
+#pragma unroll
+        for (int ks = 0; ks < BC / 16; ++ks) {
+            const bf16x8 sb = pack8(pacc[ks >> 1], 8 * (ks & 1));
+#pragma unroll
+            for (int b = 0; b < D / 32; ++b) {
+                const bf16x8 a = tr_pair(kt + toff[b] + ks * 16 * ROWB, 8 * ROWB);
+                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, acc[b], 0, 0, 0);
+            }
+        }
     }
 
     // ---- epilogue: dQ = scale * acc (lane: query lr; register r: column
@@ -448,19 +479,31 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     }
 }
 
+// Tile configurations (chosen by measurement on MI355X).
+#ifndef FA_BWD_DKDV_BR64
+#define FA_BWD_DKDV_BR64 64
+#define FA_BWD_DKDV_ST64 2
+#define FA_BWD_DQ_BC64 128
+#define FA_BWD_DQ_ST64 2
+#endif
+
 template <int D, bool CAUSAL>
-hipError_t launch_main(const BwdArgs &a, hipStream_t s) {
-    const int nkt = (int)((a.Nk + DkdvTile<D>::KEYS - 1) / DkdvTile<D>::KEYS);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(a.B * a.H * nkt)),
+hipError_t launch_main(const BwdArgs &a, float *L2, hipStream_t s) {
+    constexpr int BR = D == 64 ? FA_BWD_DKDV_BR64 : 32;
+    constexpr int ST = D == 64 ? FA_BWD_DKDV_ST64 : 2;
+    constexpr int BC = D == 64 ? FA_BWD_DQ_BC64 : 32;
+    constexpr int STQ = D == 64 ? FA_BWD_DQ_ST64 : 2;
+    const int nkt = (int)((a.Nk + DkdvCfg<D, BR, ST>::KEYS - 1) / DkdvCfg<D, BR, ST>::KEYS);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BR, ST, CAUSAL>), dim3((unsigned)(a.B * a.H * nkt)),
                        dim3(kThreads), 0, s, (const uint16_t *)a.Q, (const uint16_t *)a.K,
-                       (const uint16_t *)a.V, (const uint16_t *)a.dO, a.L, a.D, (uint16_t *)a.dK,
+                       (const uint16_t *)a.V, (const uint16_t *)a.dO, L2, a.D, (uint16_t *)a.dK,
                        (uint16_t *)a.dV, a.Nq, a.Nk, nkt, a.scale, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int nqt = (int)((a.Nq + kDqBR - 1) / kDqBR);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(a.B * a.H * nqt)),
+    const int nqt = (int)((a.Nq + DqCfg<D, BC, STQ>::BR - 1) / DqCfg<D, BC, STQ>::BR);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BC, STQ, CAUSAL>), dim3((unsigned)(a.B * a.H * nqt)),
                        dim3(kThreads), 0, s, (const uint16_t *)a.Q, (const uint16_t *)a.K,
-                       (const uint16_t *)a.V, (const uint16_t *)a.dO, a.L, a.D, (uint16_t *)a.dQ,
+                       (const uint16_t *)a.V, (const uint16_t *)a.dO, L2, a.D, (uint16_t *)a.dQ,
                        a.Nq, a.Nk, nqt, a.scale, a.scale * kLog2e);
     return hipGetLastError();
 }
@@ -471,16 +514,18 @@ hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s) {
     const int64_t rows = a.B * a.H * a.Nq;
     const int64_t chunks = rows * (a.d / 8);
     const dim3 pre_grid((unsigned)((chunks + 255) / 256));
+    float *L2 = a.L2;
     if (a.d == 128)
         hipLaunchKernelGGL(bwd_pre_kernel<128>, pre_grid, dim3(256), 0, s, (const uint16_t *)a.O,
-                           (const uint16_t *)a.dO, a.D, rows);
+                           (const uint16_t *)a.dO, a.L, a.D, L2, rows);
     else
         hipLaunchKernelGGL(bwd_pre_kernel<64>, pre_grid, dim3(256), 0, s, (const uint16_t *)a.O,
-                           (const uint16_t *)a.dO, a.D, rows);
+                           (const uint16_t *)a.dO, a.L, a.D, L2, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.d == 128) return a.causal ? launch_main<128, true>(a, s) : launch_main<128, false>(a, s);
-    return a.causal ? launch_main<64, true>(a, s) : launch_main<64, false>(a, s);
+    if (a.d == 128)
+        return a.causal ? launch_main<128, true>(a, L2, s) : launch_main<128, false>(a, L2, s);
+    return a.causal ? launch_main<64, true>(a, L2, s) : launch_main<64, false>(a, L2, s);
 }
 
 }  // namespace fa

@@ -74,7 +74,7 @@ size_t fa_bwd_workspace_size(fa_dtype dt, int64_t B, int64_t H, int64_t Nq, int6
     if (!dtype_ok(dt) || !sizes_ok(B, H, Nq, 1, d)) return 0;
     (void)d;
     const size_t rows = (size_t)(B * H * Nq);
-    return (rows * 4 + 255) / 256 * 256;
+    return 2 * ((rows * 4 + 255) / 256 * 256);
 }
 
 fa_status fa_bwd(fa_dtype dt, const void *Q, const void *K, const void *V, const void *O,
@@ -96,8 +96,9 @@ fa_status fa_bwd(fa_dtype dt, const void *Q, const void *K, const void *V, const
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (B * H * ((Nk + 63) / 64) > kMaxGrid || B * H * ((Nq + 63) / 64) > kMaxGrid)
         return FA_ERR_UNSUPPORTED;
-    fa::BwdArgs a{Q, K, V, O, dO, L, dQ, dK, dV, (float *)workspace, B, H, Nq, Nk, d, scale,
-                  causal};
+    const size_t half = need / 2;
+    fa::BwdArgs a{Q,  K,  V,  O,  dO, L,  dQ, dK, dV, (float *)workspace,
+                  (float *)((char *)workspace + half), B, H, Nq, Nk, d, scale, causal};
     return hip_status(fa::launch_bwd_bf16(a, (hipStream_t)stream));
 }
 

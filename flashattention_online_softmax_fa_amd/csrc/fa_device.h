@@ -46,6 +46,52 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// ---------------------------------------------------------------------------
+// LDS tiles streamed with global_load_lds_dwordx4.
+//
+// A tile is row-major with 16-byte chunks; chunk c of row r is stored at chunk
+// c ^ swz(r), swz(r) = 2*(r%4) + (r/4)%2.  Then 8 lanes reading the same chunk
+// of 8 consecutive rows (a 16-byte matrix-core operand per lane), and 16 lanes
+// reading 32 bytes of 4 consecutive rows (a transposed read), touch distinct
+// banks.
+// ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// Wait until at most N of this wave's vector-memory operations are pending
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8; LDS operations are also drained).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// Workgroup barrier that orders LDS accesses but does not drain outstanding
+// global loads (a ring prefetch stays in flight across it).
+__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4
+// of the 8-byte pieces addressed by lanes i/4 + 4t (t = 0..3); lanes that
+// address a 4-row x 16-column bf16 block receive its columns.
+__device__ __forceinline__ u32x2 tr_read(const uint8_t *p) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// 16-byte DMA of `src` into LDS: lane i of the wave writes dst + 16*i.
+__device__ __forceinline__ void dma16(const void *src, uint8_t *dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 0);
+}
+
+// 4-byte DMA: lane i of the wave writes dst + 4*i.
+__device__ __forceinline__ void dma4(const void *src, uint8_t *dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 4, 0, 0);
+}
+
 // Workgroups are dealt round-robin over the 8 XCDs (bid % 8).  Give each XCD
 // a contiguous range of logical tiles so that tiles sharing K/V (one head)
 // share that XCD's L2.  Identity when the grid is not a multiple of 8.

@@ -22,7 +22,8 @@ struct BwdArgs {
     const void *Q, *K, *V, *O, *dO;
     const float *L;
     void *dQ, *dK, *dV;
-    float *D;  // workspace [B][H][Nq]
+    float *D;   // workspace [B][H][Nq]: rowsum(dO * O)
+    float *L2;  // workspace [B][H][Nq]: L * log2(e)
     int64_t B, H, Nq, Nk, d;
     float scale;
     int causal;

@@ -45,10 +45,6 @@
 namespace fa {
 namespace {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr float kMargin = 8.f;         // base-2 headroom before the reference max is raised
@@ -69,26 +65,6 @@ struct Tile {
     static_assert(IPW >= 1, "tile too small for one load per wave");
     static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
 };
-
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
-
-// Wait until at most N of this wave's vector-memory operations are pending
-// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
-// 11:8; LDS operations are also drained).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
-}
-
-// Workgroup barrier that orders LDS accesses but does not drain outstanding
-// global loads (the ring prefetch stays in flight across it).
-__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
-
-__device__ __forceinline__ u32x2 tr_read(const uint8_t *p) {
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
-    return __builtin_bit_cast(u32x2, v);
-}
 
 template <int D, int QB, int BC, int ST, bool CAUSAL, bool POS_SCALE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D * QB >= 256 ? 1 : 2, 2)))
@@ -139,10 +115,8 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
             int64_t key = kv0 + ld_row[u];
             key = key < Nk ? key : Nk - 1;  // past the end: a real row, masked later
             const int blk = wave * T::IPW + u;
-            __builtin_amdgcn_global_load_lds((const void *)(Kh + key * D + ld_col[u]),
-                                             (lds_void *)(kb + blk * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(Vh + key * D + ld_col[u]),
-                                             (lds_void *)(vb + blk * 1024), 16, 0, 0);
+            dma16(Kh + key * D + ld_col[u], kb + blk * 1024);
+            dma16(Vh + key * D + ld_col[u], vb + blk * 1024);
         }
     };
 

@@ -110,8 +110,8 @@ def test_fwd_blocked_rejects(lib):
 
 
 def test_bwd_workspace_size(lib):
-    # D: 2*3*100 floats -> 2400 B -> 2560 (256-aligned)
-    assert lib.fa_bwd_workspace_size(FA_BF16, 2, 3, 100, 64) == 2560
+    # D and L*log2(e): 2*3*100 floats each -> 2400 B -> 2560 (256-aligned), twice
+    assert lib.fa_bwd_workspace_size(FA_BF16, 2, 3, 100, 64) == 2 * 2560
     assert lib.fa_bwd_workspace_size(FA_BF16, 0, 3, 100, 64) == 0
 
 
