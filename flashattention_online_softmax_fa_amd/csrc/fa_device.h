@@ -82,14 +82,30 @@ __device__ __forceinline__ u32x2 tr_read(const uint8_t *p) {
     return __builtin_bit_cast(u32x2, v);
 }
 
+// DMA of global memory into LDS (global_load_lds): lane i of the wave writes
+// `bytes` bytes at dst + bytes*i; dst must be the same in every lane.  The
+// loads are issued through inline assembly so that the compiler does not
+// track them: every ring here synchronises them itself (wait_vm, then a
+// barrier), whereas a DMA the compiler knows about makes it wait for all
+// outstanding loads before each transposed LDS read, draining the ring.
+// m0 is reserved by the compiler and cannot be named as a clobber; none of
+// the kernels uses m0 otherwise (the generated code writes it only here).
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ uint32_t lds_addr(uint8_t *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_u8 *)p);
+}
+
 // 16-byte DMA of `src` into LDS: lane i of the wave writes dst + 16*i.
 __device__ __forceinline__ void dma16(const void *src, uint8_t *dst) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 0);
+    __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :: "v"(src), "s"(lds_addr(dst)) : "memory");
 }
 
 // 4-byte DMA: lane i of the wave writes dst + 4*i.
 __device__ __forceinline__ void dma4(const void *src, uint8_t *dst) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 4, 0, 0);
+    __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                     :: "v"(src), "s"(lds_addr(dst)) : "memory");
 }
 
 // Workgroups are dealt round-robin over the 8 XCDs (bid % 8).  Give each XCD

@@ -7,12 +7,19 @@
 // after its last query under the causal mask, divides once at the end and
 // writes L = m + log l.
 //
-// Work split.  One workgroup (4 waves) per (batch*head, 128-query tile); each
-// wave owns 32 queries, whose Q rows stay in registers.  Key/value tiles of 64
-// keys stream from HBM straight into an LDS ring of STAGES slots with
+// Work split.  One workgroup (4 waves) per (batch*head, query tile); each
+// wave owns 32*QB queries, whose Q rows stay in registers.  Key/value tiles of
+// BC keys stream from HBM straight into an LDS ring of STAGES slots with
 // global_load_lds_dwordx4 (no register staging); each wave issues its share of
 // a tile and waits on its own load counter, and one barrier per tile both
-// publishes the tile and frees the slot read in the previous iteration.
+// publishes the tile and frees the slot read two steps earlier.
+//
+// Software pipeline.  Step t exponentiates the scores of tile t while the
+// matrix cores compute the scores of tile t+1, then accumulates O with tile
+// t's values; the scores of consecutive tiles alternate between two register
+// sets.  Leading tiles that need no mask for any of the wave's rows run a
+// mask-free loop; the rest (the ragged end of the keys, the causal diagonal,
+// and the idle steps of waves whose rows end earlier) run a generic one.
 //
 // LDS layout.  K and V tiles are row-major (one key per row, 16-byte chunks).
 // Chunk c of row r is stored at chunk c ^ f(r), f(r) = 2*(r%4) + (r/4)%2, which
@@ -33,13 +40,19 @@
 #include "fa_device.h"
 #include "fa_internal.h"
 
+#include <type_traits>
+
+#ifndef FA_FWD_W64
+#define FA_FWD_W64 2
+#define FA_FWD_W128 2
+#endif
 #ifndef FA_FWD_QB64
 #define FA_FWD_QB64 2
-#define FA_FWD_BC64 64
-#define FA_FWD_ST64 2
+#define FA_FWD_BC64 32
+#define FA_FWD_ST64 4
 #define FA_FWD_QB128 1
 #define FA_FWD_BC128 32
-#define FA_FWD_ST128 2
+#define FA_FWD_ST128 4
 #endif
 
 namespace fa {
@@ -63,19 +76,37 @@ struct Tile {
     static constexpr int IPW = TILEB / 1024 / kWaves;  // 1 KiB loads per wave per tensor
     static constexpr int RPI = 1024 / ROWB;          // rows per 1 KiB load
     static_assert(IPW >= 1, "tile too small for one load per wave");
-    static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
+    static_assert(STAGES >= 3 && STAGES <= 8, "ring depth");
+    static_assert(BC % 32 == 0, "32-key blocks");
 };
 
+// Wait until at most n (0 <= n <= MAX, wave-uniform) groups of PER loads of
+// this wave are still in flight.
+template <int PER, int MAX>
+__device__ __forceinline__ void wait_steps(int n) {
+    if constexpr (MAX == 0) {
+        wait_vm<0>();
+    } else {
+        if (n >= MAX)
+            wait_vm<MAX * PER>();
+        else
+            wait_steps<PER, MAX - 1>(n);
+    }
+}
+
 template <int D, int QB, int BC, int ST, bool CAUSAL, bool POS_SCALE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D * QB >= 256 ? 1 : 2, 2)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(D * QB >= 256 ? 1 : (D == 64 ? FA_FWD_W64 : FA_FWD_W128), 4)))
 void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                      const uint16_t *__restrict__ V, uint16_t *__restrict__ O,
                      float *__restrict__ L, int64_t Nq, int64_t Nk, int nqt, float c) {
     using T = Tile<D, QB, BC, ST>;
     constexpr int S = T::STAGES;
+    constexpr int KB = BC / 32;  // 32-key blocks per tile
     __shared__ __attribute__((aligned(1024))) uint8_t smem[S * 2 * T::TILEB];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, lr = lane & 31, s16 = lane & 15, G = lane >> 4;
     const int xaddr = (lane ^ 32) << 2;  // ds_bpermute address of the other half of the row
     const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -87,38 +118,58 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     const uint16_t *Kh = K + bh * Nk * D;
     const uint16_t *Vh = V + bh * Nk * D;
 
-    int64_t nkt = (Nk + BC - 1) / BC;
+    // Key tiles walked by the workgroup (every wave takes part in every ring
+    // step), by this wave (nkt_w), and the leading ones that need no mask for
+    // any row of this wave (nfull).
+    int nkt = (int)((Nk + BC - 1) / BC);
     if (CAUSAL) {
         const int64_t qlast = (q0 + T::BR < Nq ? q0 + T::BR : Nq) - 1;
         const int64_t lim = qlast / BC + 1;
-        nkt = nkt < lim ? nkt : lim;
+        nkt = nkt < lim ? nkt : (int)lim;
     }
     const int64_t qw_last = (qw0 + T::QW - 1 < Nq - 1) ? qw0 + T::QW - 1 : Nq - 1;
+    int nkt_w = 0, nfull = 0;
+    if (qw0 < Nq) {
+        nkt_w = nkt;
+        if (CAUSAL && qw_last / BC + 1 < nkt_w) nkt_w = (int)(qw_last / BC + 1);
+        int64_t f = Nk / BC;
+        if (CAUSAL && (qw0 + 1) / BC < f) f = (qw0 + 1) / BC;
+        nfull = (int)(f < nkt_w ? f : nkt_w);
+    }
 
-    // ---- per-lane constants of the ring loads: this lane fills LDS chunk
-    //      `lane` of each of its IPW 1 KiB blocks with logical chunk
-    //      (lane % CH) ^ f(row) of that row.
-    int ld_row[T::IPW], ld_col[T::IPW];
+    // ---- ring loads: this lane fills LDS chunk `lane` of each of its IPW 1 KiB
+    //      blocks with logical chunk (lane % CH) ^ f(row) of that row
+    int ld_row[T::IPW], ld_off[T::IPW];
 #pragma unroll
     for (int u = 0; u < T::IPW; ++u) {
-        const int blk = wave * T::IPW + u;
-        const int row = blk * T::RPI + lane / T::CH;
+        const int row = (wave * T::IPW + u) * T::RPI + lane / T::CH;
         ld_row[u] = row;
-        ld_col[u] = ((lane % T::CH) ^ swz(row)) * 8;
+        ld_off[u] = row * T::ROWB + ((lane % T::CH) ^ swz(row)) * 16;
     }
-    auto issue = [&](int64_t j, int st) {
-        const int64_t kv0 = j * BC;
-        uint8_t *kb = smem + st * 2 * T::TILEB;
+    auto issue = [&](int t, int st) {
+        const int64_t kv0 = (int64_t)t * BC;
+        uint8_t *kb = smem + st * 2 * T::TILEB + wave * T::IPW * 1024;
         uint8_t *vb = kb + T::TILEB;
+        const uint8_t *kt = (const uint8_t *)(Kh + kv0 * D);
+        const uint8_t *vt = (const uint8_t *)(Vh + kv0 * D);
+        if (kv0 + BC <= Nk) {
 #pragma unroll
-        for (int u = 0; u < T::IPW; ++u) {
-            int64_t key = kv0 + ld_row[u];
-            key = key < Nk ? key : Nk - 1;  // past the end: a real row, masked later
-            const int blk = wave * T::IPW + u;
-            dma16(Kh + key * D + ld_col[u], kb + blk * 1024);
-            dma16(Vh + key * D + ld_col[u], vb + blk * 1024);
+            for (int u = 0; u < T::IPW; ++u) {
+                dma16(kt + ld_off[u], kb + u * 1024);
+                dma16(vt + ld_off[u], vb + u * 1024);
+            }
+        } else {  // rows past Nk re-read the last key; they are masked
+#pragma unroll
+            for (int u = 0; u < T::IPW; ++u) {
+                const int64_t key = kv0 + ld_row[u];
+                const int64_t back = key < Nk ? 0 : (key - (Nk - 1)) * T::ROWB;
+                dma16(kt + ld_off[u] - back, kb + u * 1024);
+                dma16(vt + ld_off[u] - back, vb + u * 1024);
+            }
         }
     };
+    // wait until at most n ring steps of this wave's loads are still in flight
+    auto wait_pending = [&](int n) { wait_steps<2 * T::IPW, S - 2>(n); };
 
     // ---- per-lane constants of the LDS reads
     // K (A operand of S^T): row kb*32 + lr, logical chunk 2*ds + g
@@ -150,126 +201,143 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     }
 
     f32x16 oacc[QB][D / 32];
-    float m[QB], l[QB];
+    f32x16 sacc[QB][KB], snxt[QB][KB];  // scores of the current and the next tile
+    // m: reference maximum; l0 + l1: this lane's half of the row sum, in two
+    // chains; mt: this lane's maximum of the next tile's scores (base 2)
+    float m[QB], l0[QB], l1[QB], mt[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         m[qb] = -INFINITY;
-        l[qb] = 0.f;
+        l0[qb] = 0.f;
+        l1[qb] = 0.f;
 #pragma unroll
         for (int b = 0; b < D / 32; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[qb][b][r] = 0.f;
     }
 
+    // S^T = K_t Q^T from ring slot st; each K fragment serves all QB query blocks
+    auto scores = [&](int st, f32x16 (&acc)[QB][KB]) {
+        const uint8_t *kbase = smem + st * 2 * T::TILEB;
 #pragma unroll
-    for (int t = 0; t < S - 1; ++t)
-        if (t < nkt) issue(t, t);
-
-    for (int64_t j = 0; j < nkt; ++j) {
-        // tile j has landed for this wave once only the loads issued after it
-        // (tiles j+1 .. j+S-2) may still be pending
-        if (S >= 4 && j + 2 < nkt)
-            wait_vm<(S >= 4 ? 4 : 0) * T::IPW>();
-        else if (S >= 3 && j + 1 < nkt)
-            wait_vm<(S >= 3 ? 2 : 0) * T::IPW>();
-        else
-            wait_vm<0>();
-        lds_barrier();
-        if (j + S - 1 < nkt) issue(j + S - 1, (int)((j + S - 1) % S));
-        const uint8_t *kbase = smem + (j % S) * 2 * T::TILEB;
-        const uint8_t *vbase = kbase + T::TILEB;
-        const int64_t kv0 = j * BC;
-        const bool active = qw0 < Nq && (!CAUSAL || kv0 <= qw_last);
-        if (!active) continue;
-
-        // ---- S^T = K_j Q^T; each K fragment serves all QB query blocks
-        f32x16 sacc[QB][BC / 32];
+        for (int kb = 0; kb < KB; ++kb) {
+            bf16x8 a[D / 16];
 #pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb) {
+            for (int ds = 0; ds < D / 16; ++ds)
+                a[ds] = *(const bf16x8 *)(kbase + kb * 32 * T::ROWB + koff[ds]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[qb][kb][r] = 0.f;
+#pragma unroll
+                for (int ds = 0; ds < D / 16; ++ds)
+                    acc[qb][kb] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ds], qf[qb][ds], acc[qb][kb], 0, 0, 0);
+            }
+        }
+        if (!POS_SCALE)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int ds = 0; ds < D / 16; ++ds) {
-                const bf16x8 a = *(const bf16x8 *)(kbase + kb * 32 * T::ROWB + koff[ds]);
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    sacc[qb][kb] =
-                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ds], sacc[qb][kb], 0, 0, 0);
-            }
-        }
-        bf16x8 pf[QB][BC / 16];
+                    for (int r = 0; r < 16; ++r) acc[qb][kb][r] *= c;
+    };
+    // Mask keys past Nk, and keys after the query under causal.  Key offset of
+    // register r in this lane: kb*32 + 8*(r/4) + 4g + r%4.
+    auto mask = [&](int t, f32x16 (&acc)[QB][KB]) {
+        const int64_t kv0 = (int64_t)t * BC;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const int64_t qrow = qw0 + 32 * qb + lr;
-            if (!POS_SCALE) {
-#pragma unroll
-                for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sacc[qb][kb][r] *= c;
-            }
-            // ---- mask: keys past Nk, and keys after the query under causal.  Key
-            //      offset of register r in this lane: kb*32 + 8*(r/4) + 4g + r%4.
-            const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > qw0 + 32 * qb);
-            if (need_mask) {
+            const bool need = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > qw0 + 32 * qb);
+            if (need) {
                 int64_t lim64 = Nk - 1 - kv0;  // last visible key offset
                 if (CAUSAL && qrow - kv0 < lim64) lim64 = qrow - kv0;
                 const int lim = (int)(lim64 < -1 ? -1 : (lim64 > BC ? BC : lim64)) - 4 * g;
 #pragma unroll
-                for (int kb = 0; kb < BC / 32; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[qb][kb][r] = -INFINITY;
+                        if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) acc[qb][kb][r] = -INFINITY;
             }
-            // ---- online softmax (base 2).  m is a reference maximum: it is raised
-            //      (and the accumulator rescaled) only when the tile maximum exceeds
-            //      it by more than kMargin, so exponents stay <= 2^kMargin and most
-            //      tiles skip the rescale.  O = acc / l and L = m + log2 l do not
-            //      depend on which reference is used.
-            float mx = -INFINITY;
+        }
+    };
+    // this lane's maximum over its half of each query row of the tile, base 2
+    auto tile_max = [&](const f32x16 (&acc)[QB][KB]) {
 #pragma unroll
-            for (int kb = 0; kb < BC / 32; ++kb)
+        for (int qb = 0; qb < QB; ++qb) {
+            float v = fmaxf(acc[qb][0][0], acc[qb][0][1]);
 #pragma unroll
-                for (int r = 0; r < 16; r += 2)
-                    mx = fmaxf(mx, fmaxf(sacc[qb][kb][r], sacc[qb][kb][r + 1]));
-            // this lane's half of the tile; the other half of the row is in lane ^ 32
-            const float mt = POS_SCALE ? mx * c : mx;
-            if (__any(mt > m[qb] + kMargin)) {
-                const float mj = fmaxf(mt, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                                                        xaddr, __builtin_bit_cast(int, mt))));
+            for (int i = 2; i < 16 * KB; i += 2)  // pairs fold into three-way maxima
+                v = fmaxf(fmaxf(v, acc[qb][i / 16][i % 16]), acc[qb][i / 16][i % 16 + 1]);
+            mt[qb] = POS_SCALE ? v * c : v;
+        }
+    };
+    // Keep a value computed where it is written: the compiler would otherwise
+    // sink the row sums and maxima past the next barrier, out of the block
+    // where they overlap the matrix-core work.
+    auto pin = [](float &x) { __asm__ volatile("" : "+v"(x)); };
+
+    // One step of the walk over key tiles, software-pipelined: exponentiate
+    // tile t (scores in cur), compute the scores of tile t+1 into nxt
+    // meanwhile, and accumulate O with tile t's values.  `generic` steps mask
+    // tile t+1 where needed and handle a wave's last tile.
+    auto step = [&](int t, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB], auto generic) {
+        constexpr bool GEN = decltype(generic)::value;
+        // ---- online softmax (base 2).  m is a reference maximum: it is raised
+        //      (and the accumulator rescaled) only when the tile maximum exceeds
+        //      it by more than kMargin, so exponents stay <= 2^kMargin and most
+        //      tiles skip the rescale.  O = acc / l and L = m + log2 l do not
+        //      depend on which reference is used.  The first tile always raises
+        //      it (every row sees key 0), so m is finite afterwards.
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            if (__any(mt[qb] > m[qb] + kMargin)) {
+                // the other half of the row is in lane ^ 32
+                const float mj = fmaxf(mt[qb], __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                                        xaddr, __builtin_bit_cast(int, mt[qb]))));
                 const bool grow = mj > m[qb] + kMargin;  // same in both lanes of the row
                 const float m_new = grow ? mj : m[qb];
                 const float alpha = fast_exp2(m[qb] - m_new);  // 0 on the first tile, else <= 1
-                l[qb] *= alpha;
+                l0[qb] *= alpha;
+                l1[qb] *= alpha;
 #pragma unroll
                 for (int b = 0; b < D / 32; ++b)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) oacc[qb][b][r] *= alpha;
                 m[qb] = m_new;
             }
-            const float mref = (m[qb] == -INFINITY) ? 0.f : m[qb];
-            // ---- P^T as bf16 B operands: k-step ks uses registers 8h..8h+7 of block
-            //      ks/2, so k-slot (g, e) is key 8*(e/4) + 4g + e%4 of the step
-            float lsum = 0.f;
+        }
+        const bool next = GEN ? t + 1 < nkt_w : true;
+        if (!GEN || next) scores((t + 1) % S, nxt);
+
+        // ---- P^T as bf16 B operands: k-step ks uses registers 8h..8h+7 of block
+        //      ks/2, so k-slot (g, e) is key 8*(e/4) + 4g + e%4 of the step
+        bf16x8 pf[QB][BC / 16];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
             for (int ks = 0; ks < BC / 16; ++ks) {
                 const int kb = ks >> 1, h = ks & 1;
                 float p[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    p[e] = fast_exp2(POS_SCALE ? fmaf(sacc[qb][kb][8 * h + e], c, -mref)
-                                               : sacc[qb][kb][8 * h + e] - mref);
-                    lsum += p[e];
+                for (int e = 0; e < 8; ++e)
+                    p[e] = fast_exp2(POS_SCALE ? fmaf(cur[qb][kb][8 * h + e], c, -m[qb])
+                                               : cur[qb][kb][8 * h + e] - m[qb]);
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    l0[qb] += p[e];
+                    l1[qb] += p[e + 1];
                 }
                 const u32x4 w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                  pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
                 pf[qb][ks] = __builtin_bit_cast(bf16x8, w);
             }
-            l[qb] += lsum;  // this lane's half of the tile's keys
         }
-        // ---- O^T += V_j^T P^T; V^T read transposed in the same k-slot order and
+        // ---- O^T += V_t^T P^T; V^T read transposed in the same k-slot order and
         //      shared by the QB query blocks
+        const uint8_t *vbase = smem + (t % S) * 2 * T::TILEB + T::TILEB;
 #pragma unroll
         for (int ks = 0; ks < BC / 16; ++ks) {
 #pragma unroll
@@ -284,25 +352,79 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
                         __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][ks], oacc[qb][b], 0, 0, 0);
             }
         }
+        if (!GEN || next) {
+            if (GEN && t + 1 >= nfull) mask(t + 1, nxt);
+            tile_max(nxt);
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            pin(l0[qb]);
+            pin(l1[qb]);
+            pin(mt[qb]);
+        }
+    };
+    // ring step t: tile t+1 (keys of the next scores) has landed and is visible
+    // to every wave, the slot read in step t-1 is free, and it is refilled
+    auto ring = [&](int t) {
+        if (t + 1 < nkt) {
+            const int ahead = nkt - t - 2;  // tiles after t+1 already issued, at most S-3
+            wait_pending(ahead < S - 3 ? ahead : S - 3);
+        }
+        lds_barrier();
+        if (t + S - 1 < nkt) issue(t + S - 1, (t + S - 1) % S);
+    };
+
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t)
+        if (t < nkt) issue(t, t);
+    if (nkt > 0) {
+        wait_pending(nkt - 1 < S - 2 ? nkt - 1 : S - 2);
+        lds_barrier();
+        if (nkt_w > 0) {
+            scores(0, sacc);
+            if (nfull == 0) mask(0, sacc);
+            tile_max(sacc);
+        }
     }
+    const std::integral_constant<bool, false> plain;
+    const std::integral_constant<bool, true> generic;
+    int t = 0;
+    for (; t + 2 < nfull; t += 2) {  // tiles t .. t+2 need no mask; scores alternate
+        ring(t);
+        step(t, sacc, snxt, plain);
+        ring(t + 1);
+        step(t + 1, snxt, sacc, plain);
+    }
+    for (; t < nkt; ++t) {
+        ring(t);
+        if (t < nkt_w) {
+            step(t, sacc, snxt, generic);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) sacc[qb][kb] = snxt[qb][kb];
+        }
+    }
+    wait_vm<0>();
 
     // ---- epilogue: one division, natural-log L
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int64_t qrow = qw0 + 32 * qb + lr;
-        const float l_tot = l[qb] + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                            xaddr, __builtin_bit_cast(int, l[qb])));
+        const float lh = l0[qb] + l1[qb];
+        const float l_tot = lh + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                     xaddr, __builtin_bit_cast(int, lh)));
         if (qrow < Nq) {
             const float inv = 1.f / l_tot;
             uint16_t *orow = O + (bh * Nq + qrow) * D;
 #pragma unroll
             for (int b = 0; b < D / 32; ++b)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
+                for (int t4 = 0; t4 < 4; ++t4) {
                     const u32x2 w = {
-                        pack_bf16x2(oacc[qb][b][4 * t] * inv, oacc[qb][b][4 * t + 1] * inv),
-                        pack_bf16x2(oacc[qb][b][4 * t + 2] * inv, oacc[qb][b][4 * t + 3] * inv)};
-                    *(u32x2 *)(orow + b * 32 + 8 * t + 4 * g) = w;
+                        pack_bf16x2(oacc[qb][b][4 * t4] * inv, oacc[qb][b][4 * t4 + 1] * inv),
+                        pack_bf16x2(oacc[qb][b][4 * t4 + 2] * inv, oacc[qb][b][4 * t4 + 3] * inv)};
+                    *(u32x2 *)(orow + b * 32 + 8 * t4 + 4 * g) = w;
                 }
             if (g == 0) L[bh * Nq + qrow] = (m[qb] + log2f(l_tot)) * kLn2;
         }
