@@ -45,8 +45,12 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16 &v, int r0) {
     return __builtin_bit_cast(bf16x8, w);
 }
 
-__device__ __forceinline__ bf16x8 tr_pair(const uint8_t *p, int row_bytes8) {
-    const u32x2 lo = tr_read(p), hi = tr_read(p + row_bytes8);
+// Two transposed reads (rows 4g.. and 8 + 4g.. of a 16-row step) -> bf16x8.
+// `off` is tr_off<ROWB>(lane, b, 0); the rows 8 further down start at
+// (off ^ 32) + 8 * ROWB, since both swizzles satisfy swz(r + 8) = swz(r) ^ 2.
+template <int ROWB>
+__device__ __forceinline__ bf16x8 tr_pair(const uint8_t *base, int off) {
+    const u32x2 lo = tr_read(base + off), hi = tr_read(base + ((off ^ 32) + 8 * ROWB));
     const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
     return __builtin_bit_cast(bf16x8, w);
 }
@@ -90,20 +94,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
         Dv[row] = s;
         L2[row] = L[row] * kLog2e;
     }
-}
-
-// Per-lane LDS offsets shared by both kernels, for a tile of ROWB-byte rows:
-//   row_off(ds): 16-byte operand of row (lane%32), logical chunk 2*ds + g;
-//   tr_off(b):   transposed read at rows 4g + lane%16/4 (+16k, +8), columns
-//                32b + 16*((lane/16)%2) + 4*(lane%4).
-__device__ __forceinline__ int row_off(int lr, int g, int ds, int ROWB) {
-    return lr * ROWB + 16 * ((2 * ds + g) ^ swz(lr));
-}
-__device__ __forceinline__ int tr_off(int lane, int b, int ROWB) {
-    const int g = lane >> 5, s = lane & 15, G = lane >> 4;
-    const int row = 4 * g + (s >> 2);
-    const int chunk = 4 * b + 2 * (G & 1) + ((s >> 1) & 1);
-    return row * ROWB + 16 * (chunk ^ (((s >> 2) << 1) | g)) + 8 * (s & 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -163,7 +153,7 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     for (int u = 0; u < T::IPW; ++u) {
         const int row = (wave * T::IPW + u) * T::RPI + lane / T::CH;
         ld_row[u] = row;
-        ld_col[u] = ((lane % T::CH) ^ swz(row)) * 8;
+        ld_col[u] = (lane % T::CH) ^ swz<ROWB>(row);
     }
     auto issue = [&](int it, int st) {
         const int64_t q0 = (int64_t)it * BR;
@@ -174,8 +164,8 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
             int64_t q = q0 + ld_row[u];
             q = q < Nq ? q : Nq - 1;  // past the end: a real row, masked in compute
             const int blk = wave * T::IPW + u;
-            dma16(Qh + q * D + ld_col[u], qb + blk * 1024);
-            dma16(dOh + q * D + ld_col[u], ob + blk * 1024);
+            dma16(Qh + q * D + ld_col[u] * 8, qb + blk * 1024);
+            dma16(dOh + q * D + ld_col[u] * 8, ob + blk * 1024);
         }
         if (wave < 2) {
             int64_t q = q0 + lane;
@@ -186,9 +176,9 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
 
     int qoff[D / 16], toff[D / 32];
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) qoff[ds] = row_off(lr, g, ds, ROWB);
+    for (int ds = 0; ds < D / 16; ++ds) qoff[ds] = chunk_off<ROWB>(lr, 2 * ds + g);
 #pragma unroll
-    for (int b = 0; b < D / 32; ++b) toff[b] = tr_off(lane, b, ROWB);
+    for (int b = 0; b < D / 32; ++b) toff[b] = tr_off<ROWB>(lane, b, 0);
 
     f32x16 dvacc[D / 32], dkacc[D / 32];
 #pragma unroll
@@ -279,9 +269,9 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
             const bf16x8 sb = pack8(pacc[kq >> 1], 8 * (kq & 1));
 #pragma unroll
             for (int b = 0; b < D / 32; ++b) {
-                const int off = toff[b] + kq * 16 * ROWB;
-                const bf16x8 ao = tr_pair(ot + off, 8 * ROWB);
-                const bf16x8 aq = tr_pair(qt + off, 8 * ROWB);
+                const int off = kq * 16 * ROWB;
+                const bf16x8 ao = tr_pair<ROWB>(ot + off, toff[b]);
+                const bf16x8 aq = tr_pair<ROWB>(qt + off, toff[b]);
                 dvacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb, dvacc[b], 0, 0, 0);
                 dkacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb, dkacc[b], 0, 0, 0);
             }
@@ -371,7 +361,7 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     for (int u = 0; u < T::IPW; ++u) {
         const int row = (wave * T::IPW + u) * T::RPI + lane / T::CH;
         ld_row[u] = row;
-        ld_col[u] = ((lane % T::CH) ^ swz(row)) * 8;
+        ld_col[u] = (lane % T::CH) ^ swz<ROWB>(row);
     }
     auto issue = [&](int64_t j, int st) {
         const int64_t kv0 = j * BC;
@@ -382,15 +372,15 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
             int64_t key = kv0 + ld_row[u];
             key = key < Nk ? key : Nk - 1;  // past the end: a real row, masked later
             const int blk = wave * T::IPW + u;
-            dma16(Kh + key * D + ld_col[u], kb + blk * 1024);
-            dma16(Vh + key * D + ld_col[u], vb + blk * 1024);
+            dma16(Kh + key * D + ld_col[u] * 8, kb + blk * 1024);
+            dma16(Vh + key * D + ld_col[u] * 8, vb + blk * 1024);
         }
     };
     int koff[D / 16], toff[D / 32];
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) koff[ds] = row_off(lr, g, ds, ROWB);
+    for (int ds = 0; ds < D / 16; ++ds) koff[ds] = chunk_off<ROWB>(lr, 2 * ds + g);
 #pragma unroll
-    for (int b = 0; b < D / 32; ++b) toff[b] = tr_off(lane, b, ROWB);
+    for (int b = 0; b < D / 32; ++b) toff[b] = tr_off<ROWB>(lane, b, 0);
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -458,7 +448,7 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
             const bf16x8 sb = pack8(pacc[ks >> 1], 8 * (ks & 1));
 #pragma unroll
             for (int b = 0; b < D / 32; ++b) {
-                const bf16x8 a = tr_pair(kt + toff[b] + ks * 16 * ROWB, 8 * ROWB);
+                const bf16x8 a = tr_pair<ROWB>(kt + ks * 16 * ROWB, toff[b]);
                 acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, acc[b], 0, 0, 0);
             }
         }

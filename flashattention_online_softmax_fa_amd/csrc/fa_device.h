@@ -50,16 +50,47 @@ __device__ __forceinline__ float wave_sum(float v) {
 // LDS tiles streamed with global_load_lds_dwordx4.
 //
 // A tile is row-major with 16-byte chunks; chunk c of row r is stored at chunk
-// c ^ swz(r), swz(r) = 2*(r%4) + (r/4)%2.  Then 8 lanes reading the same chunk
-// of 8 consecutive rows (a 16-byte matrix-core operand per lane), and 16 lanes
-// reading 32 bytes of 4 consecutive rows (a transposed read), touch distinct
-// banks.
+// c ^ swz<ROWB>(r).  The gfx950 LDS serves a 16-byte read to 16 lanes per
+// clock from 64 four-byte banks (one 256-byte bank row), and a transposed
+// 8-byte read from 4 rows x 32 bytes per 16 lanes.  The two access patterns
+// of the attention kernels are
+//   row reads:        16 lanes read the same logical chunk of 16 consecutive
+//                     rows (one matrix-core operand per lane);
+//   transposed reads: lanes read 32 bytes (two chunks) of 4 consecutive rows
+//                     starting at a multiple of 4, with the chunk pair 2-aligned;
+// the swizzles below put every lane of such a group on its own banks:
+//   128-byte rows (two per bank row): swz = 4*((r>>1)&1) + ((r>>2)&3), which
+//     takes 8 distinct values on the even and on the odd rows of any 16;
+//   256-byte rows: swz = 4*(r&3) + ((r>>2)&3), 16 distinct values on any 16
+//     consecutive rows, and distinct 4-aligned chunk groups on 4 rows.
+// Both are unchanged by adding 16 rows, so tiles may be indexed with
+// immediates in steps of 16 rows.
 // ---------------------------------------------------------------------------
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+template <int ROWB>
+__device__ __forceinline__ int swz(int r) {
+    static_assert(ROWB == 128 || ROWB == 256, "row size");
+    return ROWB == 128 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
+}
+
+// Byte offset of logical chunk c of row r.
+template <int ROWB>
+__device__ __forceinline__ int chunk_off(int r, int c) {
+    return r * ROWB + 16 * (c ^ swz<ROWB>(r));
+}
+
+// Transposed-read base of this lane: rows 8h + 4*(lane/32) + (lane%16)/4 and
+// columns 32b + 16*((lane/16)%2) + 4*(lane%4); with the read at +16k rows.
+template <int ROWB>
+__device__ __forceinline__ int tr_off(int lane, int b, int h) {
+    const int g = lane >> 5, s = lane & 15, G = lane >> 4;
+    const int row = 8 * h + 4 * g + (s >> 2);
+    const int chunk = 4 * b + 2 * (G & 1) + ((s >> 1) & 1);
+    return chunk_off<ROWB>(row, chunk) + 8 * (s & 1);
+}
 
 // Wait until at most N of this wave's vector-memory operations are pending
 // (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt

@@ -22,10 +22,9 @@
 // and the idle steps of waves whose rows end earlier) run a generic one.
 //
 // LDS layout.  K and V tiles are row-major (one key per row, 16-byte chunks).
-// Chunk c of row r is stored at chunk c ^ f(r), f(r) = 2*(r%4) + (r/4)%2, which
-// makes both access patterns below free of bank conflicts: 8 lanes reading the
-// same chunk of 8 consecutive rows, and 16 lanes reading 32 bytes of 4
-// consecutive rows.
+// Chunks are XOR-swizzled per row (swz in fa_device.h) so that both access
+// patterns below are free of bank conflicts: 16 lanes reading the same chunk
+// of 16 consecutive rows, and 16 lanes reading 32 bytes of 4 consecutive rows.
 //
 // Matrix-core layout (v_mfma_f32_32x32x16_bf16, C[m][n] with lane = n).  The
 // wave computes S^T = K Q^T, so each lane's 16 accumulator values belong to
@@ -144,7 +143,7 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     for (int u = 0; u < T::IPW; ++u) {
         const int row = (wave * T::IPW + u) * T::RPI + lane / T::CH;
         ld_row[u] = row;
-        ld_off[u] = row * T::ROWB + ((lane % T::CH) ^ swz(row)) * 16;
+        ld_off[u] = chunk_off<T::ROWB>(row, lane % T::CH);
     }
     auto issue = [&](int t, int st) {
         const int64_t kv0 = (int64_t)t * BC;
@@ -175,15 +174,14 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     // K (A operand of S^T): row kb*32 + lr, logical chunk 2*ds + g
     int koff[D / 16];
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) koff[ds] = lr * T::ROWB + 16 * ((2 * ds + g) ^ swz(lr));
-    // V^T (A operand of O^T, transposed read): rows 16ks + 4g + 8h + s/4,
-    // columns 32b + 16*(G&1) + 4*(s%4)
-    int voff[D / 32];
+    for (int ds = 0; ds < D / 16; ++ds) koff[ds] = chunk_off<T::ROWB>(lr, 2 * ds + g);
+    // V^T (A operand of O^T, transposed read): rows 16ks + 8h + 4g + (lane%16)/4,
+    // columns 32b + 16*((lane/16)%2) + 4*(lane%4)
+    int voff[D / 32][2];
 #pragma unroll
     for (int b = 0; b < D / 32; ++b) {
-        const int row = 4 * g + (s16 >> 2);
-        const int chunk = 4 * b + 2 * (G & 1) + ((s16 >> 1) & 1);
-        voff[b] = row * T::ROWB + 16 * (chunk ^ (((s16 >> 2) << 1) | g)) + 8 * (s16 & 1);
+        voff[b][0] = tr_off<T::ROWB>(lane, b, 0);
+        voff[b][1] = tr_off<T::ROWB>(lane, b, 1);
     }
 
     // ---- Q fragments: B operands of S^T = K Q^T (lane: query lr of each block)
@@ -342,8 +340,8 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         for (int ks = 0; ks < BC / 16; ++ks) {
 #pragma unroll
             for (int b = 0; b < D / 32; ++b) {
-                const uint8_t *p = vbase + voff[b] + ks * 16 * T::ROWB;
-                const u32x2 lo = tr_read(p), hi = tr_read(p + 8 * T::ROWB);
+                const uint8_t *p = vbase + ks * 16 * T::ROWB;
+                const u32x2 lo = tr_read(p + voff[b][0]), hi = tr_read(p + voff[b][1]);
                 const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
                 const bf16x8 a = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
