@@ -1,8 +1,8 @@
 """MI355X (gfx950) FlashAttention: a thin Python binding over libfa.so.
 
-The functions named like the C entry points (``fa_fwd``, ``fa_fwd_blocked``,
-``fa_bwd``, ``fa_bwd_workspace_size``, ``fa_decode_split``,
-``fa_merge_states``, ``fa_status_str``) only check and marshal torch tensors
+The functions named like the C entry points (``fa_fwd``, ``fa_fwd_offset``,
+``fa_fwd_blocked``, ``fa_bwd``, ``fa_bwd_offset``, ``fa_bwd_workspace_size``,
+``fa_decode_split``, ``fa_merge_states``, ``fa_status_str``) only check and marshal torch tensors
 into the C ABI of ``include/fa.h``; every step of the computation runs in the
 library's HIP kernels.  ``forward``, ``backward`` and ``decode`` additionally
 allocate the outputs with torch before calling them.
@@ -34,23 +34,28 @@ _lib = ctypes.CDLL(LIB_PATH)
 _vp, _i64, _f32, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
 _lib.fa_fwd.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _int,
                         _vp]
+_lib.fa_fwd_offset.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                               _f32, _i64, _vp]
 _lib.fa_fwd_blocked.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                 _f32, _int, _i64, _vp]
 _lib.fa_bwd_workspace_size.argtypes = [_int, _i64, _i64, _i64, _i64]
 _lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
 _lib.fa_bwd.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                         _i64, _i64, _i64, _i64, _i64, _f32, _int, _vp]
+_lib.fa_bwd_offset.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64, _f32, _i64, _vp]
 _lib.fa_decode_split.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                  _i64, _i64, _f32, _vp]
 _lib.fa_merge_states.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                  _vp]
 _lib.fa_status_str.argtypes = [_int]
 _lib.fa_status_str.restype = ctypes.c_char_p
-for _f in ("fa_fwd", "fa_fwd_blocked", "fa_bwd", "fa_decode_split", "fa_merge_states"):
+for _f in ("fa_fwd", "fa_fwd_offset", "fa_fwd_blocked", "fa_bwd", "fa_bwd_offset",
+           "fa_decode_split", "fa_merge_states"):
     getattr(_lib, _f).restype = _int
 
-EXPORTS = ("fa_fwd", "fa_fwd_blocked", "fa_bwd_workspace_size", "fa_bwd", "fa_decode_split",
-           "fa_merge_states", "fa_status_str")
+EXPORTS = ("fa_fwd", "fa_fwd_offset", "fa_fwd_blocked", "fa_bwd_workspace_size", "fa_bwd",
+           "fa_bwd_offset", "fa_decode_split", "fa_merge_states", "fa_status_str")
 
 
 class FaError(RuntimeError):
@@ -114,6 +119,16 @@ def fa_fwd(q, k, v, o, lse, scale=None, causal=False, stream=None) -> None:
                        _scale(d, scale), int(bool(causal)), _stream(stream)), "fa_fwd")
 
 
+def fa_fwd_offset(q, k, v, o, lse, q_start, scale=None, stream=None) -> None:
+    B, H, Nq, d = _bhnd(q)
+    Nk = _bhnd(k)[2]
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    _check(_lib.fa_fwd_offset(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq,
+                              Nk, d, _scale(d, scale), int(q_start), _stream(stream)),
+           "fa_fwd_offset")
+
+
 def fa_fwd_blocked(q, k, v, o, lse, kv_block, scale=None, causal=False, stream=None) -> None:
     B, H, Nq, d = _bhnd(q)
     Nk = _bhnd(k)[2]
@@ -137,6 +152,17 @@ def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, workspace, scale=None, causal=False,
                        _scale(d, scale), int(bool(causal)), _stream(stream)), "fa_bwd")
 
 
+def fa_bwd_offset(q, k, v, o, lse, do, dq, dk, dv, workspace, q_start, scale=None,
+                  stream=None) -> None:
+    B, H, Nq, d = _bhnd(q)
+    Nk = _bhnd(k)[2]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.fa_bwd_offset(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, Nq,
+                              Nk, d, _scale(d, scale), int(q_start), _stream(stream)),
+           "fa_bwd_offset")
+
+
 def fa_decode_split(q, k, v, part_m, part_l, part_o, n_split, scale=None, stream=None) -> None:
     B, H, Nq, d = _bhnd(q)
     Nk = _bhnd(k)[2]
@@ -156,24 +182,34 @@ def fa_merge_states(part_m, part_l, part_o, o, lse, stream=None) -> None:
 # ---------------------------------------------------------------------------
 # Convenience wrappers that allocate outputs with torch.
 # ---------------------------------------------------------------------------
-def forward(q, k, v, scale=None, causal=False, kv_block=None, stream=None):
-    """(O, L) for Q [B,H,Nq,d], K, V [B,H,Nk,d]; L is fp32 [B,H,Nq]."""
+def forward(q, k, v, scale=None, causal=False, kv_block=None, stream=None, q_start=None):
+    """(O, L) for Q [B,H,Nq,d], K, V [B,H,Nk,d]; L is fp32 [B,H,Nq].
+
+    With ``q_start`` set, the attention is causal with query row i at key
+    position q_start + i (``causal`` is then implied)."""
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
-    if kv_block is None:
+    if q_start is not None:
+        if kv_block is not None:
+            raise ValueError("kv_block and q_start cannot be combined")
+        fa_fwd_offset(q, k, v, o, lse, q_start, scale, stream)
+    elif kv_block is None:
         fa_fwd(q, k, v, o, lse, scale, causal, stream)
     else:
         fa_fwd_blocked(q, k, v, o, lse, kv_block, scale, causal, stream)
     return o, lse
 
 
-def backward(q, k, v, o, lse, do, scale=None, causal=False, stream=None):
+def backward(q, k, v, o, lse, do, scale=None, causal=False, stream=None, q_start=None):
     """(dQ, dK, dV) of <O, dO>; O and L from forward() with the same arguments."""
     B, H, Nq, d = q.shape
     ws = torch.empty(fa_bwd_workspace_size(q.dtype, B, H, Nq, d), dtype=torch.uint8,
                      device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, scale, causal, stream)
+    if q_start is not None:
+        fa_bwd_offset(q, k, v, o, lse, do, dq, dk, dv, ws, q_start, scale, stream)
+    else:
+        fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, scale, causal, stream)
     return dq, dk, dv
 
 

@@ -120,7 +120,7 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
                      const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
                      const float *__restrict__ L2, const float *__restrict__ Dv,
                      uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int64_t Nq, int64_t Nk,
-                     int nkt, float scale, float c) {
+                     int64_t qoff, int nkt, float scale, float c) {
     using T = DkdvCfg<D, BR, ST>;
     constexpr int QB = T::QB, ROWB = T::ROWB;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * T::STAGEB];
@@ -174,9 +174,9 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         }
     };
 
-    int qoff[D / 16], toff[D / 32];
+    int roff[D / 16], toff[D / 32];
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) qoff[ds] = chunk_off<ROWB>(lr, 2 * ds + g);
+    for (int ds = 0; ds < D / 16; ++ds) roff[ds] = chunk_off<ROWB>(lr, 2 * ds + g);
 #pragma unroll
     for (int b = 0; b < D / 32; ++b) toff[b] = tr_off<ROWB>(lane, b, 0);
 
@@ -189,9 +189,10 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
             dkacc[b][r] = 0.f;
         }
 
-    // query tiles that can see this key tile
+    // query tiles that can see this key tile (causal: query q sees keys
+    // 0 .. q + qoff)
     const int nqt = (int)((Nq + BR - 1) / BR);
-    const int it0 = CAUSAL ? (int)(k0 / BR) : 0;
+    const int it0 = CAUSAL ? (int)(k0 - qoff > 0 ? (k0 - qoff) / BR : 0) : 0;
 #pragma unroll
     for (int t = 0; t < ST - 1; ++t)
         if (it0 + t < nqt) issue(it0 + t, t);
@@ -209,7 +210,7 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         lds_barrier();
         if (it + ST - 1 < nqt) issue(it + ST - 1, (idx + ST - 1) % ST);
         const int64_t q0 = (int64_t)it * BR;
-        const bool active = kw0 < Nk && (!CAUSAL || q0 + BR - 1 >= kw0);
+        const bool active = kw0 < Nk && (!CAUSAL || q0 + BR - 1 + qoff >= kw0);
         if (!active) continue;
         const uint8_t *qt = smem + (idx % ST) * T::STAGEB;
         const uint8_t *ot = qt + T::TILEB;
@@ -228,7 +229,7 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
             }
 #pragma unroll
             for (int ds = 0; ds < D / 16; ++ds) {
-                const int off = qb * 32 * ROWB + qoff[ds];
+                const int off = qb * 32 * ROWB + roff[ds];
                 const bf16x8 aq = *(const bf16x8 *)(qt + off);
                 const bf16x8 ao = *(const bf16x8 *)(ot + off);
                 sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ds], sacc[qb], 0, 0, 0);
@@ -238,7 +239,7 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         // ---- P = exp2(S c - L2), dS = P (dP - D); zero past Nq, past Nk, and
         //      (causal) where the key comes after the query
         const bool need_mask =
-            (q0 + BR > Nq) || (kw0 + 32 > Nk) || (CAUSAL && q0 < kw0 + 31);
+            (q0 + BR > Nq) || (kw0 + 32 > Nk) || (CAUSAL && q0 + qoff < kw0 + 31);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
@@ -252,7 +253,7 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
                     float p = fast_exp2(fmaf(sacc[qb][r], c, -lv[e]));
                     if (need_mask) {
                         const int64_t q = q0 + qi + e;
-                        if (q >= Nq || mykey >= Nk || (CAUSAL && mykey > q)) p = 0.f;
+                        if (q >= Nq || mykey >= Nk || (CAUSAL && mykey > q + qoff)) p = 0.f;
                     }
                     sacc[qb][r] = p;
                     pacc[qb][r] = p * (pacc[qb][r] - dv[e]);
@@ -319,8 +320,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                    const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
                    const float *__restrict__ L2, const float *__restrict__ Dv,
-                   uint16_t *__restrict__ dQ, int64_t Nq, int64_t Nk, int nqt, float scale,
-                   float c) {
+                   uint16_t *__restrict__ dQ, int64_t Nq, int64_t Nk, int64_t qoff, int nqt,
+                   float scale, float c) {
     using T = DqCfg<D, BC, ST>;
     constexpr int ROWB = T::ROWB;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * 2 * T::TILEB];
@@ -340,7 +341,7 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     int64_t nkt = (Nk + BC - 1) / BC;
     if (CAUSAL) {
         const int64_t qlast = (q0 + T::BR < Nq ? q0 + T::BR : Nq) - 1;
-        const int64_t lim = qlast / BC + 1;
+        const int64_t lim = (qlast + qoff) / BC + 1;
         nkt = nkt < lim ? nkt : lim;
     }
     const int64_t qw_last = (qw0 + 31 < Nq - 1) ? qw0 + 31 : Nq - 1;
@@ -400,7 +401,7 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
         lds_barrier();
         if (j + ST - 1 < nkt) issue(j + ST - 1, (int)((j + ST - 1) % ST));
         const int64_t kv0 = j * BC;
-        const bool active = qw0 < Nq && (!CAUSAL || kv0 <= qw_last);
+        const bool active = qw0 < Nq && (!CAUSAL || kv0 <= qw_last + qoff);
         if (!active) continue;
         const uint8_t *kt = smem + (j % ST) * 2 * T::TILEB;
         const uint8_t *vt = kt + T::TILEB;
@@ -425,11 +426,11 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
             }
         }
         // ---- P = exp2(S c - L2), dS = P (dP - D), both per lane
-        const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > qw0);
+        const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > qw0 + qoff);
         int lim = BC;
         if (need_mask) {
             int64_t lim64 = Nk - 1 - kv0;  // last visible key offset
-            if (CAUSAL && qrow - kv0 < lim64) lim64 = qrow - kv0;
+            if (CAUSAL && qrow + qoff - kv0 < lim64) lim64 = qrow + qoff - kv0;
             lim = (int)(lim64 < -1 ? -1 : (lim64 > BC ? BC : lim64)) - 4 * g;
         }
 #pragma unroll
@@ -479,7 +480,9 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 
 template <int D, bool CAUSAL>
 hipError_t launch_main(const BwdArgs &a, float *L2, hipStream_t s) {
-    constexpr int BR = D == 64 ? FA_BWD_DKDV_BR64 : 32;
+    // the non-causal d = 64 instance keeps 32-query tiles: with 64 it needs more
+    // than 256 registers
+    constexpr int BR = D == 64 && CAUSAL ? FA_BWD_DKDV_BR64 : 32;
     constexpr int ST = D == 64 ? FA_BWD_DKDV_ST64 : 2;
     constexpr int BC = D == 64 ? FA_BWD_DQ_BC64 : 32;
     constexpr int STQ = D == 64 ? FA_BWD_DQ_ST64 : 2;
@@ -487,14 +490,14 @@ hipError_t launch_main(const BwdArgs &a, float *L2, hipStream_t s) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, BR, ST, CAUSAL>), dim3((unsigned)(a.B * a.H * nkt)),
                        dim3(kThreads), 0, s, (const uint16_t *)a.Q, (const uint16_t *)a.K,
                        (const uint16_t *)a.V, (const uint16_t *)a.dO, L2, a.D, (uint16_t *)a.dK,
-                       (uint16_t *)a.dV, a.Nq, a.Nk, nkt, a.scale, a.scale * kLog2e);
+                       (uint16_t *)a.dV, a.Nq, a.Nk, a.q_start, nkt, a.scale, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nqt = (int)((a.Nq + DqCfg<D, BC, STQ>::BR - 1) / DqCfg<D, BC, STQ>::BR);
     hipLaunchKernelGGL((bwd_dq_kernel<D, BC, STQ, CAUSAL>), dim3((unsigned)(a.B * a.H * nqt)),
                        dim3(kThreads), 0, s, (const uint16_t *)a.Q, (const uint16_t *)a.K,
                        (const uint16_t *)a.V, (const uint16_t *)a.dO, L2, a.D, (uint16_t *)a.dQ,
-                       a.Nq, a.Nk, nqt, a.scale, a.scale * kLog2e);
+                       a.Nq, a.Nk, a.q_start, nqt, a.scale, a.scale * kLog2e);
     return hipGetLastError();
 }
 

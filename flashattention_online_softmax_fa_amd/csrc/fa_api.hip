@@ -29,18 +29,23 @@ constexpr int64_t kMaxGrid = 2147483647;
 
 fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// Largest accepted query offset of the causal mask; keeps q_start + Nq far
+// from int64 overflow in the kernels' tile arithmetic.
+constexpr int64_t kMaxQStart = int64_t(1) << 40;
+
 fa_status fwd_common(fa_dtype dt, const void *Q, const void *K, const void *V, void *O, float *L,
                      int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
-                     int causal, int64_t kv_block, void *stream) {
+                     int causal, int64_t q_start, int64_t kv_block, void *stream) {
     if (!dtype_ok(dt)) return FA_ERR_INVALID_ARG;
     if (!sizes_ok(B, H, Nq, Nk, d)) return FA_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (q_start < 0 || q_start > kMaxQStart) return FA_ERR_INVALID_ARG;
     const uintptr_t al = dt == FA_BF16 ? 16 : 4;
     if (!aligned(Q, al) || !aligned(K, al) || !aligned(V, al) || !aligned(O, al) ||
         !aligned(L, 4))
         return FA_ERR_INVALID_ARG;
-    fa::FwdArgs a{Q, K, V, O, L, B, H, Nq, Nk, d, scale, causal, kv_block};
+    fa::FwdArgs a{Q, K, V, O, L, B, H, Nq, Nk, d, scale, causal, kv_block, q_start};
     if (dt == FA_F32) {
         if (d > 128) return FA_ERR_UNSUPPORTED;
         if ((B * H * Nq + 3) / 4 > kMaxGrid) return FA_ERR_UNSUPPORTED;
@@ -52,6 +57,12 @@ fa_status fwd_common(fa_dtype dt, const void *Q, const void *K, const void *V, v
     return hip_status(fa::launch_fwd_bf16(a, (hipStream_t)stream));
 }
 
+fa_status bwd_common(fa_dtype dt, const void *Q, const void *K, const void *V, const void *O,
+                     const float *L, const void *dO, void *dQ, void *dK, void *dV,
+                     void *workspace, size_t ws_bytes, int64_t B, int64_t H, int64_t Nq,
+                     int64_t Nk, int64_t d, float scale, int causal, int64_t q_start,
+                     void *stream);
+
 }  // namespace
 
 extern "C" {
@@ -59,7 +70,13 @@ extern "C" {
 fa_status fa_fwd(fa_dtype dt, const void *Q, const void *K, const void *V, void *O, float *L,
                  int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
                  int causal, void *stream) {
-    return fwd_common(dt, Q, K, V, O, L, B, H, Nq, Nk, d, scale, causal, 0, stream);
+    return fwd_common(dt, Q, K, V, O, L, B, H, Nq, Nk, d, scale, causal, 0, 0, stream);
+}
+
+fa_status fa_fwd_offset(fa_dtype dt, const void *Q, const void *K, const void *V, void *O,
+                        float *L, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                        float scale, int64_t q_start, void *stream) {
+    return fwd_common(dt, Q, K, V, O, L, B, H, Nq, Nk, d, scale, 1, q_start, 0, stream);
 }
 
 fa_status fa_fwd_blocked(fa_dtype dt, const void *Q, const void *K, const void *V, void *O,
@@ -67,7 +84,7 @@ fa_status fa_fwd_blocked(fa_dtype dt, const void *Q, const void *K, const void *
                          float scale, int causal, int64_t kv_block, void *stream) {
     if (dt != FA_F32) return dt == FA_BF16 ? FA_ERR_UNSUPPORTED : FA_ERR_INVALID_ARG;
     if (kv_block < 1 || kv_block > 256) return FA_ERR_INVALID_ARG;
-    return fwd_common(dt, Q, K, V, O, L, B, H, Nq, Nk, d, scale, causal, kv_block, stream);
+    return fwd_common(dt, Q, K, V, O, L, B, H, Nq, Nk, d, scale, causal, 0, kv_block, stream);
 }
 
 size_t fa_bwd_workspace_size(fa_dtype dt, int64_t B, int64_t H, int64_t Nq, int64_t d) {
@@ -81,10 +98,32 @@ fa_status fa_bwd(fa_dtype dt, const void *Q, const void *K, const void *V, const
                  const float *L, const void *dO, void *dQ, void *dK, void *dV, void *workspace,
                  size_t ws_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                  float scale, int causal, void *stream) {
+    return bwd_common(dt, Q, K, V, O, L, dO, dQ, dK, dV, workspace, ws_bytes, B, H, Nq, Nk, d,
+                      scale, causal, 0, stream);
+}
+
+fa_status fa_bwd_offset(fa_dtype dt, const void *Q, const void *K, const void *V, const void *O,
+                        const float *L, const void *dO, void *dQ, void *dK, void *dV,
+                        void *workspace, size_t ws_bytes, int64_t B, int64_t H, int64_t Nq,
+                        int64_t Nk, int64_t d, float scale, int64_t q_start, void *stream) {
+    return bwd_common(dt, Q, K, V, O, L, dO, dQ, dK, dV, workspace, ws_bytes, B, H, Nq, Nk, d,
+                      scale, 1, q_start, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+fa_status bwd_common(fa_dtype dt, const void *Q, const void *K, const void *V, const void *O,
+                     const float *L, const void *dO, void *dQ, void *dK, void *dV,
+                     void *workspace, size_t ws_bytes, int64_t B, int64_t H, int64_t Nq,
+                     int64_t Nk, int64_t d, float scale, int causal, int64_t q_start,
+                     void *stream) {
     if (!dtype_ok(dt)) return FA_ERR_INVALID_ARG;
     if (!sizes_ok(B, H, Nq, Nk, d)) return FA_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (q_start < 0 || q_start > kMaxQStart) return FA_ERR_INVALID_ARG;
     const uintptr_t al = dt == FA_BF16 ? 16 : 4;
     if (!aligned(Q, al) || !aligned(K, al) || !aligned(V, al) || !aligned(O, al) ||
         !aligned(dO, al) || !aligned(dQ, al) || !aligned(dK, al) || !aligned(dV, al) ||
@@ -98,9 +137,13 @@ fa_status fa_bwd(fa_dtype dt, const void *Q, const void *K, const void *V, const
         return FA_ERR_UNSUPPORTED;
     const size_t half = need / 2;
     fa::BwdArgs a{Q,  K,  V,  O,  dO, L,  dQ, dK, dV, (float *)workspace,
-                  (float *)((char *)workspace + half), B, H, Nq, Nk, d, scale, causal};
+                  (float *)((char *)workspace + half), B, H, Nq, Nk, d, scale, causal, q_start};
     return hip_status(fa::launch_bwd_bf16(a, (hipStream_t)stream));
 }
+
+}  // namespace
+
+extern "C" {
 
 fa_status fa_decode_split(fa_dtype dt, const void *Q, const void *K, const void *V,
                           float *part_m, float *part_l, float *part_o, int64_t B, int64_t H,

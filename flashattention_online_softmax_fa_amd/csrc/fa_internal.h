@@ -16,6 +16,7 @@ struct FwdArgs {
     float scale;
     int causal;
     int64_t kv_block;  // fp32 path: keys per online-softmax step
+    int64_t q_start;   // causal: query row i sits at key position q_start + i
 };
 
 struct BwdArgs {
@@ -27,6 +28,7 @@ struct BwdArgs {
     int64_t B, H, Nq, Nk, d;
     float scale;
     int causal;
+    int64_t q_start;  // causal: query row i sits at key position q_start + i
 };
 
 struct DecodeArgs {

@@ -98,7 +98,8 @@ __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D * QB >= 256 ? 1 : (D == 64 ? FA_FWD_W64 : FA_FWD_W128), 4)))
 void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                      const uint16_t *__restrict__ V, uint16_t *__restrict__ O,
-                     float *__restrict__ L, int64_t Nq, int64_t Nk, int nqt, float c) {
+                     float *__restrict__ L, int64_t Nq, int64_t Nk, int64_t qoff, int nqt,
+                     float c) {
     using T = Tile<D, QB, BC, ST>;
     constexpr int S = T::STAGES;
     constexpr int KB = BC / 32;  // 32-key blocks per tile
@@ -119,20 +120,21 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
 
     // Key tiles walked by the workgroup (every wave takes part in every ring
     // step), by this wave (nkt_w), and the leading ones that need no mask for
-    // any row of this wave (nfull).
+    // any row of this wave (nfull).  Under causal, query row q sees keys
+    // 0 .. q + qoff.
     int nkt = (int)((Nk + BC - 1) / BC);
     if (CAUSAL) {
         const int64_t qlast = (q0 + T::BR < Nq ? q0 + T::BR : Nq) - 1;
-        const int64_t lim = qlast / BC + 1;
+        const int64_t lim = (qlast + qoff) / BC + 1;
         nkt = nkt < lim ? nkt : (int)lim;
     }
     const int64_t qw_last = (qw0 + T::QW - 1 < Nq - 1) ? qw0 + T::QW - 1 : Nq - 1;
     int nkt_w = 0, nfull = 0;
     if (qw0 < Nq) {
         nkt_w = nkt;
-        if (CAUSAL && qw_last / BC + 1 < nkt_w) nkt_w = (int)(qw_last / BC + 1);
+        if (CAUSAL && (qw_last + qoff) / BC + 1 < nkt_w) nkt_w = (int)((qw_last + qoff) / BC + 1);
         int64_t f = Nk / BC;
-        if (CAUSAL && (qw0 + 1) / BC < f) f = (qw0 + 1) / BC;
+        if (CAUSAL && (qw0 + qoff + 1) / BC < f) f = (qw0 + qoff + 1) / BC;
         nfull = (int)(f < nkt_w ? f : nkt_w);
     }
 
@@ -248,10 +250,10 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const int64_t qrow = qw0 + 32 * qb + lr;
-            const bool need = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > qw0 + 32 * qb);
+            const bool need = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > qw0 + 32 * qb + qoff);
             if (need) {
                 int64_t lim64 = Nk - 1 - kv0;  // last visible key offset
-                if (CAUSAL && qrow - kv0 < lim64) lim64 = qrow - kv0;
+                if (CAUSAL && qrow + qoff - kv0 < lim64) lim64 = qrow + qoff - kv0;
                 const int lim = (int)(lim64 < -1 ? -1 : (lim64 > BC ? BC : lim64)) - 4 * g;
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
@@ -438,11 +440,11 @@ hipError_t launch_d(const FwdArgs &a, hipStream_t s) {
     if (a.scale > 0.f)
         hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BC, ST, CAUSAL, true>), grid, dim3(kThreads), 0, s,
                            (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
-                           (uint16_t *)a.O, a.L, a.Nq, a.Nk, nqt, c);
+                           (uint16_t *)a.O, a.L, a.Nq, a.Nk, a.q_start, nqt, c);
     else
         hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BC, ST, CAUSAL, false>), grid, dim3(kThreads), 0,
                            s, (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
-                           (uint16_t *)a.O, a.L, a.Nq, a.Nk, nqt, c);
+                           (uint16_t *)a.O, a.L, a.Nq, a.Nk, a.q_start, nqt, c);
     return hipGetLastError();
 }
 

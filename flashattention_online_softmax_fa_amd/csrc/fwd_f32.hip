@@ -24,7 +24,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float *__restrict__ 
                                                       const float *__restrict__ V,
                                                       float *__restrict__ O, float *__restrict__ L,
                                                       int64_t rows, int64_t Nq, int64_t Nk, int d,
-                                                      float c, int causal, int step) {
+                                                      float c, int causal, int64_t qoff,
+                                                      int step) {
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
     if (row >= rows) return;  // wave-uniform; the kernel has no block barrier
@@ -32,7 +33,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float *__restrict__ 
     const float *q = Q + row * d;
     const float *Kh = K + bh * Nk * d;
     const float *Vh = V + bh * Nk * d;
-    const int64_t nvis = causal ? (i + 1 < Nk ? i + 1 : Nk) : Nk;
+    // causal: keys 0 .. qoff + i are visible (qoff >= 0, so at least key 0)
+    const int64_t nvis = causal ? (qoff + i + 1 < Nk ? qoff + i + 1 : Nk) : Nk;
 
     float m = -INFINITY, l = 0.f, acc0 = 0.f, acc1 = 0.f;
     for (int64_t start = 0; start < nvis; start += step) {
@@ -92,7 +94,8 @@ hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t s) {
     if (step > kMaxStep) step = kMaxStep;
     hipLaunchKernelGGL(fwd_f32_kernel, dim3((unsigned)blocks), dim3(64 * kWaves), 0, s,
                        (const float *)a.Q, (const float *)a.K, (const float *)a.V, (float *)a.O,
-                       a.L, rows, a.Nq, a.Nk, (int)a.d, a.scale * kLog2e, a.causal, step);
+                       a.L, rows, a.Nq, a.Nk, (int)a.d, a.scale * kLog2e, a.causal, a.q_start,
+                       step);
     return hipGetLastError();
 }
 

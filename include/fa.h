@@ -79,6 +79,22 @@ fa_status fa_fwd(fa_dtype dt, const void *Q, const void *K, const void *V, void 
                  int causal, void *stream);
 
 /*
+ * fa_fwd_offset -- causal forward with the queries placed at key positions
+ * q_start .. q_start + Nq - 1: key j is visible to query row i iff
+ * j <= q_start + i.  q_start = Nk - Nq aligns the last query with the last key
+ * (bottom-right causal: a chunk of new tokens attending to a cache that ends
+ * with them); q_start = 0 is fa_fwd with causal = 1.
+ * Source: standard_attention and flash_forward (attention_kernels.py), whose
+ * causal mask compares absolute positions q_start + i and j, and skips key
+ * tiles that start after the tile's last absolute query position.
+ *   q_start  0 <= q_start <= 2^40 (every row then sees key 0); larger values
+ *            than Nk - 1 leave every key visible.  Other arguments as fa_fwd.
+ */
+fa_status fa_fwd_offset(fa_dtype dt, const void *Q, const void *K, const void *V, void *O,
+                        float *L, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                        float scale, int64_t q_start, void *stream);
+
+/*
  * fa_fwd_blocked -- fp32 forward whose online-softmax step is exactly
  * `kv_block` keys (1 <= kv_block <= 256), for checking block-size invariance.
  * Source: TiledAttention (model.py) and tiled (lab.py): the result does not
@@ -115,6 +131,20 @@ fa_status fa_bwd(fa_dtype dt, const void *Q, const void *K, const void *V, const
                  const float *L, const void *dO, void *dQ, void *dK, void *dV, void *workspace,
                  size_t ws_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                  float scale, int causal, void *stream);
+
+/*
+ * fa_bwd_offset -- backward of fa_fwd_offset: the same causal mask with
+ * query row i at key position q_start + i.  Key tiles that no query can see
+ * get dK = dV = 0.
+ * Source: flash_backward (attention_kernels.py) with the mask of
+ * standard_attention at offset q_start.
+ *   q_start  as fa_fwd_offset; O and L must come from fa_fwd_offset with the
+ *            same q_start.  Other arguments, workspace included, as fa_bwd.
+ */
+fa_status fa_bwd_offset(fa_dtype dt, const void *Q, const void *K, const void *V, const void *O,
+                        const float *L, const void *dO, void *dQ, void *dK, void *dV,
+                        void *workspace, size_t ws_bytes, int64_t B, int64_t H, int64_t Nq,
+                        int64_t Nk, int64_t d, float scale, int64_t q_start, void *stream);
 
 /*
  * fa_decode_split -- first pass of split-KV decoding (Flash-Decoding).

@@ -28,12 +28,15 @@ def lib():
     lib = ctypes.CDLL(SO)
     vp, i64, f32, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
     lib.fa_fwd.argtypes = [i, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i, vp]
+    lib.fa_fwd_offset.argtypes = [i, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i64, vp]
     lib.fa_fwd_blocked.argtypes = [i, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i, i64,
                                    vp]
     lib.fa_bwd_workspace_size.argtypes = [i, i64, i64, i64, i64]
     lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64,
                            i64, i64, i64, f32, i, vp]
+    lib.fa_bwd_offset.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64,
+                                  i64, i64, i64, i64, f32, i64, vp]
     lib.fa_decode_split.argtypes = [i, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32,
                                     vp]
     lib.fa_merge_states.argtypes = [i, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp]
@@ -43,7 +46,8 @@ def lib():
 
 
 def test_header_declares_the_calls():
-    assert _declared() == sorted(["fa_fwd", "fa_fwd_blocked", "fa_bwd_workspace_size", "fa_bwd",
+    assert _declared() == sorted(["fa_fwd", "fa_fwd_offset", "fa_fwd_blocked",
+                                  "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_offset",
                                   "fa_decode_split", "fa_merge_states", "fa_status_str"])
 
 
@@ -100,6 +104,20 @@ def fwd(lib, **kw):
 ])
 def test_fwd_rejects(lib, kw, want):
     assert fwd(lib, **kw) == want
+
+
+def test_offset_rejects(lib):
+    args = (P, P, P, P, P, 1, 1, 8, 8, 64, 0.125)
+    assert lib.fa_fwd_offset(FA_BF16, *args, -1, None) == FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_offset(FA_BF16, *args, (1 << 40) + 1, None) == FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_offset(FA_BF16, *args[:-2], 96, 0.125, 3, None) == FA_ERR_UNSUPPORTED
+    assert lib.fa_fwd_offset(FA_F32, P, P, P, P, P, 1, 1, 8, 8, 129, 0.125, 3,
+                             None) == FA_ERR_UNSUPPORTED
+    need = lib.fa_bwd_workspace_size(FA_BF16, 1, 1, 8, 64)
+    bargs = (P, P, P, P, P, P, P, P, P, P, need, 1, 1, 8, 8, 64, 0.125)
+    assert lib.fa_bwd_offset(FA_BF16, *bargs, -5, None) == FA_ERR_INVALID_ARG
+    assert lib.fa_bwd_offset(FA_F32, *bargs, 2, None) == FA_ERR_UNSUPPORTED
+    assert lib.fa_bwd_offset(FA_BF16, *bargs[:-1], float("nan"), 2, None) == FA_ERR_INVALID_ARG
 
 
 def test_fwd_blocked_rejects(lib):

@@ -428,3 +428,56 @@ def test_planted_mistake_is_caught(tmp_path, golden, name):
 
 def test_unplanted_build_passes(golden):
     assert _pins_pass(golden)
+
+
+# ---------------------------------------------------------------------------
+# Causal offset q_start (standard_attention / flash_forward: query row i sits
+# at absolute position q_start + i).  Pinned to the q_start = 0 path, which is
+# pinned above, through the chunked-prefill identity: the rows s .. s+m-1 of
+# the causal attention over the whole sequence are the offset attention of
+# those m queries at q_start = s over the same keys.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("s,m", [(0, 7), (5, 9), (17, 3), (23, 1)])
+def test_offset_is_chunked_prefill(s, m):
+    B, H, N, d = 1, 2, 24, 8
+    Q, K, V = _rand((B, H, N, d), 31), _rand((B, H, N, d), 32), _rand((B, H, N, d), 33)
+    scale = 0.3
+    O_full, L_full = oracle.dense_fwd(Q, K, V, scale, causal=True)
+    O, L = oracle.dense_fwd(Q[:, :, s:s + m], K, V, scale, causal=True, q_start=s)
+    np.testing.assert_allclose(O, O_full[:, :, s:s + m], atol=1e-13, rtol=0)
+    np.testing.assert_allclose(L, L_full[:, :, s:s + m], atol=1e-13, rtol=0)
+    # the online recurrence follows the same mask
+    O2, L2 = oracle.online_fwd(Q[:, :, s:s + m], K, V, scale, causal=True, block=5, q_start=s)
+    np.testing.assert_allclose(O2, O, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(L2, L, atol=1e-12, rtol=0)
+
+
+def test_offset_past_the_keys_is_unmasked():
+    """q_start >= Nk - 1: every row sees every key (non-causal result)."""
+    Q, K, V = _rand((1, 1, 6, 4), 41), _rand((1, 1, 10, 4), 42), _rand((1, 1, 10, 4), 43)
+    O0, L0 = oracle.dense_fwd(Q, K, V, 0.5, causal=False)
+    for q_start in (9, 50):
+        O, L = oracle.dense_fwd(Q, K, V, 0.5, causal=True, q_start=q_start)
+        np.testing.assert_allclose(O, O0, atol=1e-14, rtol=0)
+        np.testing.assert_allclose(L, L0, atol=1e-14, rtol=0)
+
+
+@pytest.mark.parametrize("s,m", [(4, 8), (13, 11)])
+def test_offset_backward_is_chunked_prefill(s, m):
+    """Gradient of <O_rows, dO_rows> for the rows s .. s+m-1: the offset
+    backward over those rows equals the full causal backward with dO = 0 on
+    every other row (dK, dV), and its dQ is those rows of the full dQ."""
+    B, H, N, d = 1, 1, 24, 6
+    Q, K, V = _rand((B, H, N, d), 51), _rand((B, H, N, d), 52), _rand((B, H, N, d), 53)
+    dO = np.zeros((B, H, N, d))
+    dO[:, :, s:s + m] = _rand((B, H, m, d), 54)
+    scale = 0.4
+    full = oracle.dense_bwd(Q, K, V, dO, scale, causal=True)
+    part = oracle.dense_bwd(Q[:, :, s:s + m], K, V, dO[:, :, s:s + m], scale, causal=True,
+                            q_start=s)
+    np.testing.assert_allclose(part["dK"], full["dK"], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(part["dV"], full["dV"], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(part["dQ"], full["dQ"][:, :, s:s + m], atol=1e-12, rtol=0)
+    # keys after the last query's position get no gradient
+    last = s + m - 1
+    assert np.all(part["dK"][:, :, last + 1:] == 0) and np.all(part["dV"][:, :, last + 1:] == 0)
