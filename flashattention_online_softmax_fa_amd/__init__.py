@@ -2,7 +2,8 @@
 
 The functions named like the C entry points (``fa_fwd``, ``fa_fwd_offset``,
 ``fa_fwd_blocked``, ``fa_bwd``, ``fa_bwd_offset``, ``fa_bwd_workspace_size``,
-``fa_decode_split``, ``fa_merge_states``, ``fa_status_str``) only check and marshal torch tensors
+``fa_decode_split``, ``fa_decode_split_offset``, ``fa_merge_states``,
+``fa_status_str``) only check and marshal torch tensors
 into the C ABI of ``include/fa.h``; every step of the computation runs in the
 library's HIP kernels.  ``forward``, ``backward`` and ``decode`` additionally
 allocate the outputs with torch before calling them.
@@ -46,16 +47,19 @@ _lib.fa_bwd_offset.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp
                                ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64, _f32, _i64, _vp]
 _lib.fa_decode_split.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                  _i64, _i64, _f32, _vp]
+_lib.fa_decode_split_offset.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                        _i64, _i64, _i64, _f32, _i64, _vp]
 _lib.fa_merge_states.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                  _vp]
 _lib.fa_status_str.argtypes = [_int]
 _lib.fa_status_str.restype = ctypes.c_char_p
 for _f in ("fa_fwd", "fa_fwd_offset", "fa_fwd_blocked", "fa_bwd", "fa_bwd_offset",
-           "fa_decode_split", "fa_merge_states"):
+           "fa_decode_split", "fa_decode_split_offset", "fa_merge_states"):
     getattr(_lib, _f).restype = _int
 
 EXPORTS = ("fa_fwd", "fa_fwd_offset", "fa_fwd_blocked", "fa_bwd_workspace_size", "fa_bwd",
-           "fa_bwd_offset", "fa_decode_split", "fa_merge_states", "fa_status_str")
+           "fa_bwd_offset", "fa_decode_split", "fa_decode_split_offset", "fa_merge_states",
+           "fa_status_str")
 
 
 class FaError(RuntimeError):
@@ -171,6 +175,16 @@ def fa_decode_split(q, k, v, part_m, part_l, part_o, n_split, scale=None, stream
                                 _stream(stream)), "fa_decode_split")
 
 
+def fa_decode_split_offset(q, k, v, part_m, part_l, part_o, n_split, q_start, scale=None,
+                           stream=None) -> None:
+    B, H, Nq, d = _bhnd(q)
+    Nk = _bhnd(k)[2]
+    _check(_lib.fa_decode_split_offset(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(part_m),
+                                       _ptr(part_l), _ptr(part_o), B, H, Nq, Nk, d, int(n_split),
+                                       _scale(d, scale), int(q_start), _stream(stream)),
+           "fa_decode_split_offset")
+
+
 def fa_merge_states(part_m, part_l, part_o, o, lse, stream=None) -> None:
     B, H, Nq, n_split = part_m.shape
     d = o.shape[-1]
@@ -213,14 +227,18 @@ def backward(q, k, v, o, lse, do, scale=None, causal=False, stream=None, q_start
     return dq, dk, dv
 
 
-def decode(q, k, v, n_split, scale=None, stream=None, out_dtype=None):
-    """Split-KV decoding: returns (O, L, (part_m, part_l, part_o))."""
+def decode(q, k, v, n_split, scale=None, stream=None, out_dtype=None, q_start=None):
+    """Split-KV decoding: returns (O, L, (part_m, part_l, part_o)).  With
+    ``q_start`` the Nq query rows attend causally from key position q_start + i."""
     B, H, Nq, d = q.shape
     dev = q.device
     pm = torch.empty((B, H, Nq, n_split), dtype=torch.float32, device=dev)
     pl = torch.empty_like(pm)
     po = torch.empty((B, H, Nq, n_split, d), dtype=torch.float32, device=dev)
-    fa_decode_split(q, k, v, pm, pl, po, n_split, scale, stream)
+    if q_start is None:
+        fa_decode_split(q, k, v, pm, pl, po, n_split, scale, stream)
+    else:
+        fa_decode_split_offset(q, k, v, pm, pl, po, n_split, q_start, scale, stream)
     o = torch.empty((B, H, Nq, d), dtype=out_dtype or q.dtype, device=dev)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
     fa_merge_states(pm, pl, po, o, lse, stream)

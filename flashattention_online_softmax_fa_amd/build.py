@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 SO = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_api.hip", "fwd_f32.hip", "fwd_bf16.hip", "bwd.hip", "decode.hip"]
+SOURCES = ["fa_api.hip", "fwd_f32.hip", "fwd_bf16.hip", "bwd.hip", "bwd_f32.hip", "decode.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -9,7 +9,9 @@
 // LDS at the end with the merge rule.  Nothing here is a dense contraction
 // (one query row), so it runs on the vector ALUs; the bound is HBM bandwidth.
 // Source: flash_decode and state_of_scores (attention_kernels.py): split
-// bounds, per-split summaries, and the empty split as the identity.
+// bounds, per-split summaries, and the empty split as the identity.  With
+// the causal offset, row i of the Nq new tokens sees keys 0 .. q_start + i
+// (the mask of standard_attention), so a split can be empty for some rows.
 //
 // Pass 2 (merge_states_kernel): one workgroup per row folds the n_split
 // summaries with merge_states (attention_kernels.py): largest m, rebase both
@@ -55,7 +57,8 @@ template <int D>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, float *__restrict__ part_m, float *__restrict__ part_l,
-    float *__restrict__ part_o, int64_t Nq, int64_t Nk, int64_t n_split, float c) {
+    float *__restrict__ part_o, int64_t Nq, int64_t Nk, int64_t n_split, float c, int causal,
+    int64_t qoff) {
     constexpr int LPK = D / 8;       // lanes per key row
     constexpr int KPI = 64 / LPK;    // key rows per wave instruction
     constexpr int NG = kDecWaves * KPI;  // lane groups per workgroup
@@ -65,7 +68,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const int64_t item = blockIdx.x;
     const int64_t row = item / n_split, split = item % n_split;
     const int64_t bh = row / Nq;
-    const int64_t j0 = Nk * split / n_split, j1 = Nk * (split + 1) / n_split;
+    const int64_t j0 = Nk * split / n_split;
+    int64_t j1 = Nk * (split + 1) / n_split;
+    // causal over the new tokens: row i (of Nq) sees keys 0 .. qoff + i
+    if (causal && qoff + row % Nq + 1 < j1) j1 = qoff + row % Nq + 1;
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int grp = lane / LPK, sub = lane % LPK;
     const int g = wave * KPI + grp;  // this lane group's id in the workgroup
@@ -191,11 +197,13 @@ hipError_t launch_decode_split_bf16(const DecodeArgs &a, hipStream_t s) {
     if (a.d == 128)
         hipLaunchKernelGGL(decode_split_kernel<128>, grid, dim3(kDecThreads), 0, s,
                            (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
-                           a.part_m, a.part_l, a.part_o, a.Nq, a.Nk, a.n_split, c);
+                           a.part_m, a.part_l, a.part_o, a.Nq, a.Nk, a.n_split, c, a.causal,
+                           a.q_start);
     else
         hipLaunchKernelGGL(decode_split_kernel<64>, grid, dim3(kDecThreads), 0, s,
                            (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
-                           a.part_m, a.part_l, a.part_o, a.Nq, a.Nk, a.n_split, c);
+                           a.part_m, a.part_l, a.part_o, a.Nq, a.Nk, a.n_split, c, a.causal,
+                           a.q_start);
     return hipGetLastError();
 }
 

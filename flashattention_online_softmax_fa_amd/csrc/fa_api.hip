@@ -63,6 +63,30 @@ fa_status bwd_common(fa_dtype dt, const void *Q, const void *K, const void *V, c
                      int64_t Nk, int64_t d, float scale, int causal, int64_t q_start,
                      void *stream);
 
+fa_status decode_common(fa_dtype dt, const void *Q, const void *K, const void *V, float *part_m,
+                        float *part_l, float *part_o, int64_t B, int64_t H, int64_t Nq,
+                        int64_t Nk, int64_t d, int64_t n_split, float scale, int causal,
+                        int64_t q_start, void *stream) {
+    if (!dtype_ok(dt)) return FA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H, Nq, Nk, d)) return FA_ERR_INVALID_ARG;
+    if (n_split < 1 || n_split > (int64_t(1) << 20)) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (q_start < 0 || q_start > kMaxQStart) return FA_ERR_INVALID_ARG;
+    const uintptr_t al = dt == FA_BF16 ? 16 : 4;
+    if (!aligned(Q, al) || !aligned(K, al) || !aligned(V, al) || !aligned(part_m, 4) ||
+        !aligned(part_l, 4) || !aligned(part_o, 4))
+        return FA_ERR_INVALID_ARG;
+    if (B * H * Nq > kMaxGrid / n_split) return FA_ERR_UNSUPPORTED;
+    fa::DecodeArgs a{Q, K, V, part_m, part_l, part_o, B, H, Nq, Nk, d, n_split, scale, causal,
+                     q_start};
+    if (dt == FA_F32) {
+        if (d > 128) return FA_ERR_UNSUPPORTED;
+        return hip_status(fa::launch_decode_split_f32(a, (hipStream_t)stream));
+    }
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    return hip_status(fa::launch_decode_split_bf16(a, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,13 +155,18 @@ fa_status bwd_common(fa_dtype dt, const void *Q, const void *K, const void *V, c
         return FA_ERR_INVALID_ARG;
     const size_t need = fa_bwd_workspace_size(dt, B, H, Nq, d);
     if (ws_bytes < need) return FA_ERR_INVALID_ARG;
-    if (dt != FA_BF16) return FA_ERR_UNSUPPORTED;
-    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-    if (B * H * ((Nk + 63) / 64) > kMaxGrid || B * H * ((Nq + 63) / 64) > kMaxGrid)
-        return FA_ERR_UNSUPPORTED;
     const size_t half = need / 2;
     fa::BwdArgs a{Q,  K,  V,  O,  dO, L,  dQ, dK, dV, (float *)workspace,
                   (float *)((char *)workspace + half), B, H, Nq, Nk, d, scale, causal, q_start};
+    if (dt == FA_F32) {
+        if (d > 128) return FA_ERR_UNSUPPORTED;
+        if ((B * H * Nq + 3) / 4 > kMaxGrid || (B * H * Nk + 3) / 4 > kMaxGrid)
+            return FA_ERR_UNSUPPORTED;
+        return hip_status(fa::launch_bwd_f32(a, (hipStream_t)stream));
+    }
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (B * H * ((Nk + 63) / 64) > kMaxGrid || B * H * ((Nq + 63) / 64) > kMaxGrid)
+        return FA_ERR_UNSUPPORTED;
     return hip_status(fa::launch_bwd_bf16(a, (hipStream_t)stream));
 }
 
@@ -149,19 +178,16 @@ fa_status fa_decode_split(fa_dtype dt, const void *Q, const void *K, const void 
                           float *part_m, float *part_l, float *part_o, int64_t B, int64_t H,
                           int64_t Nq, int64_t Nk, int64_t d, int64_t n_split, float scale,
                           void *stream) {
-    if (!dtype_ok(dt)) return FA_ERR_INVALID_ARG;
-    if (!sizes_ok(B, H, Nq, Nk, d)) return FA_ERR_INVALID_ARG;
-    if (n_split < 1 || n_split > (int64_t(1) << 20)) return FA_ERR_INVALID_ARG;
-    if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
-    const uintptr_t al = dt == FA_BF16 ? 16 : 4;
-    if (!aligned(Q, al) || !aligned(K, al) || !aligned(V, al) || !aligned(part_m, 4) ||
-        !aligned(part_l, 4) || !aligned(part_o, 4))
-        return FA_ERR_INVALID_ARG;
-    if (dt != FA_BF16) return FA_ERR_UNSUPPORTED;
-    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-    if (B * H * Nq > kMaxGrid / n_split) return FA_ERR_UNSUPPORTED;
-    fa::DecodeArgs a{Q, K, V, part_m, part_l, part_o, B, H, Nq, Nk, d, n_split, scale};
-    return hip_status(fa::launch_decode_split_bf16(a, (hipStream_t)stream));
+    return decode_common(dt, Q, K, V, part_m, part_l, part_o, B, H, Nq, Nk, d, n_split, scale, 0,
+                         0, stream);
+}
+
+fa_status fa_decode_split_offset(fa_dtype dt, const void *Q, const void *K, const void *V,
+                                 float *part_m, float *part_l, float *part_o, int64_t B,
+                                 int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t n_split,
+                                 float scale, int64_t q_start, void *stream) {
+    return decode_common(dt, Q, K, V, part_m, part_l, part_o, B, H, Nq, Nk, d, n_split, scale, 1,
+                         q_start, stream);
 }
 
 fa_status fa_merge_states(fa_dtype dt, const float *part_m, const float *part_l,

@@ -36,6 +36,8 @@ struct DecodeArgs {
     float *part_m, *part_l, *part_o;
     int64_t B, H, Nq, Nk, d, n_split;
     float scale;
+    int causal;       // query row i sees keys 0 .. q_start + i only
+    int64_t q_start;
 };
 
 struct MergeArgs {
@@ -50,6 +52,8 @@ hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s);
 hipError_t launch_decode_split_bf16(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_split_f32(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_bwd_f32(const BwdArgs &a, hipStream_t s);
 hipError_t launch_merge_states(const MergeArgs &a, hipStream_t s);
 
 }  // namespace fa

@@ -120,10 +120,13 @@ size_t fa_bwd_workspace_size(fa_dtype dt, int64_t B, int64_t H, int64_t Nq, int6
  * are accumulated per key tile; dQ is accumulated per query tile by a
  * second pass that recomputes S and dP (no atomic additions), so the
  * result is deterministic.
- *   dt         FA_BF16 only (FA_F32 returns FA_ERR_UNSUPPORTED); d in {64, 128}.
+ *   dt         FA_BF16: bf16 tensors on matrix cores, d in {64, 128}.
+ *              FA_F32:  fp32 tensors on the vector ALUs, 1 <= d <= 128 (meant
+ *              for exact checks at small sizes).
+ *   dQ, dK, dV have the dtype of Q.
  *   O, L       the forward's outputs for the same Q, K, V, scale, causal.
  *   dO         upstream gradient [B][H][Nq][d] bf16.
- *   dQ, dK, dV outputs, bf16, fully overwritten.
+ *   dQ, dK, dV outputs, fully overwritten.
  *   workspace  device buffer of at least fa_bwd_workspace_size() bytes,
  *              256-byte aligned; its contents on entry do not matter.
  */
@@ -153,8 +156,9 @@ fa_status fa_bwd_offset(fa_dtype dt, const void *Q, const void *K, const void *V
  * [floor(Nk*s/n_split), floor(Nk*(s+1)/n_split)); each split is summarised
  * independently as (m, l, o) with m = max score, l = sum exp(s - m),
  * o = sum exp(s - m) V (unnormalised).  An empty split (n_split > Nk) gives
- * (-inf, 0, 0).  No causal mask.
- *   dt      FA_BF16 only; d = 128 or 64.  Q [B][H][Nq][d], K, V [B][H][Nk][d].
+ * (-inf, 0, 0).  No causal mask (see fa_decode_split_offset).
+ *   dt      FA_BF16: d = 128 or 64.  FA_F32: 1 <= d <= 128 (vector ALUs).
+ *           Q [B][H][Nq][d], K, V [B][H][Nk][d].
  *   part_m, part_l  outputs [B][H][Nq][n_split] fp32 (m in natural-log units,
  *                   i.e. the scale is applied).
  *   part_o          output [B][H][Nq][n_split][d] fp32.
@@ -164,6 +168,21 @@ fa_status fa_decode_split(fa_dtype dt, const void *Q, const void *K, const void 
                           float *part_m, float *part_l, float *part_o, int64_t B, int64_t H,
                           int64_t Nq, int64_t Nk, int64_t d, int64_t n_split, float scale,
                           void *stream);
+
+/*
+ * fa_decode_split_offset -- fa_decode_split for Nq new tokens that attend
+ * causally: query row i sits at key position q_start + i and sees keys
+ * 0 .. q_start + i only (q_start = Nk - Nq: the tokens are the last Nq keys
+ * of the cache).  A split with no visible key for a row gives (-inf, 0, 0)
+ * for that row; merging it changes nothing.
+ * Source: flash_decode (attention_kernels.py) with the causal mask of
+ * standard_attention at offset q_start.
+ *   q_start  0 <= q_start <= 2^40.  Other arguments as fa_decode_split.
+ */
+fa_status fa_decode_split_offset(fa_dtype dt, const void *Q, const void *K, const void *V,
+                                 float *part_m, float *part_l, float *part_o, int64_t B,
+                                 int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t n_split,
+                                 float scale, int64_t q_start, void *stream);
 
 /*
  * fa_merge_states -- second pass: fold n_split states per row with the merge

@@ -39,6 +39,8 @@ def lib():
                                   i64, i64, i64, i64, f32, i64, vp]
     lib.fa_decode_split.argtypes = [i, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32,
                                     vp]
+    lib.fa_decode_split_offset.argtypes = [i, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                           i64, f32, i64, vp]
     lib.fa_merge_states.argtypes = [i, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp]
     lib.fa_status_str.argtypes = [i]
     lib.fa_status_str.restype = ctypes.c_char_p
@@ -48,7 +50,8 @@ def lib():
 def test_header_declares_the_calls():
     assert _declared() == sorted(["fa_fwd", "fa_fwd_offset", "fa_fwd_blocked",
                                   "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_offset",
-                                  "fa_decode_split", "fa_merge_states", "fa_status_str"])
+                                  "fa_decode_split", "fa_decode_split_offset", "fa_merge_states",
+                                  "fa_status_str"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -116,7 +119,7 @@ def test_offset_rejects(lib):
     need = lib.fa_bwd_workspace_size(FA_BF16, 1, 1, 8, 64)
     bargs = (P, P, P, P, P, P, P, P, P, P, need, 1, 1, 8, 8, 64, 0.125)
     assert lib.fa_bwd_offset(FA_BF16, *bargs, -5, None) == FA_ERR_INVALID_ARG
-    assert lib.fa_bwd_offset(FA_F32, *bargs, 2, None) == FA_ERR_UNSUPPORTED
+    assert lib.fa_bwd_offset(FA_F32, *bargs[:-2], 129, 0.125, 2, None) == FA_ERR_UNSUPPORTED
     assert lib.fa_bwd_offset(FA_BF16, *bargs[:-1], float("nan"), 2, None) == FA_ERR_INVALID_ARG
 
 
@@ -147,8 +150,8 @@ def bwd(lib, **kw):
     (dict(ws_bytes=100), FA_ERR_INVALID_ARG),
     (dict(dO=NULL), FA_ERR_INVALID_ARG),
     (dict(scale=float("-inf")), FA_ERR_INVALID_ARG),
-    (dict(d=32), FA_ERR_UNSUPPORTED),
-    (dict(dt=FA_F32), FA_ERR_UNSUPPORTED),
+    (dict(d=32), FA_ERR_UNSUPPORTED),             # bf16 tiles exist for d = 64, 128
+    (dict(dt=FA_F32, d=129), FA_ERR_UNSUPPORTED),  # fp32 path: d <= 128
 ])
 def test_bwd_rejects(lib, kw, want):
     assert bwd(lib, **kw) == want
@@ -162,7 +165,11 @@ def test_decode_rejects(lib):
     assert call(Q=NULL) == FA_ERR_INVALID_ARG
     assert call(pm=P + 1) == FA_ERR_INVALID_ARG
     assert call(d=80) == FA_ERR_UNSUPPORTED
-    assert call(dt=FA_F32) == FA_ERR_UNSUPPORTED
+    assert call(dt=FA_F32, d=200) == FA_ERR_UNSUPPORTED
+    assert lib.fa_decode_split_offset(FA_BF16, P, P, P, P, P, P, 1, 1, 1, 64, 64, 4, 0.1, -1,
+                                      None) == FA_ERR_INVALID_ARG
+    assert lib.fa_decode_split_offset(FA_BF16, P, P, P, P, P, P, 1, 1, 1, 64, 96, 4, 0.1, 63,
+                                      None) == FA_ERR_UNSUPPORTED
 
 
 def test_merge_rejects(lib):
