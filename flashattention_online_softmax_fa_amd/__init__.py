@@ -21,7 +21,7 @@ import os
 
 import torch
 
-_HERE = os.path.dirname(os.path.abspath(__file__))
+_PKG_DIR = _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
@@ -31,31 +31,38 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
                       "(hipcc --offload-arch=gfx950)")
 
-_lib = ctypes.CDLL(LIB_PATH)
 _vp, _i64, _f32, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
-_lib.fa_fwd.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _int,
-                        _vp]
-_lib.fa_fwd_offset.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
-                               _f32, _i64, _vp]
-_lib.fa_fwd_blocked.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
-                                _f32, _int, _i64, _vp]
-_lib.fa_bwd_workspace_size.argtypes = [_int, _i64, _i64, _i64, _i64]
-_lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
-_lib.fa_bwd.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
-                        _i64, _i64, _i64, _i64, _i64, _f32, _int, _vp]
-_lib.fa_bwd_offset.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                               ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64, _f32, _i64, _vp]
-_lib.fa_decode_split.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
-                                 _i64, _i64, _f32, _vp]
-_lib.fa_decode_split_offset.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
-                                        _i64, _i64, _i64, _f32, _i64, _vp]
-_lib.fa_merge_states.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
-                                 _vp]
-_lib.fa_status_str.argtypes = [_int]
-_lib.fa_status_str.restype = ctypes.c_char_p
-for _f in ("fa_fwd", "fa_fwd_offset", "fa_fwd_blocked", "fa_bwd", "fa_bwd_offset",
-           "fa_decode_split", "fa_decode_split_offset", "fa_merge_states"):
-    getattr(_lib, _f).restype = _int
+
+
+def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Argument and result types of the include/fa.h entry points of `lib`."""
+    lib.fa_fwd.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
+                           _int, _vp]
+    lib.fa_fwd_offset.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                  _f32, _i64, _vp]
+    lib.fa_fwd_blocked.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                   _f32, _int, _i64, _vp]
+    lib.fa_bwd_workspace_size.argtypes = [_int, _i64, _i64, _i64, _i64]
+    lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                           ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64, _f32, _int, _vp]
+    lib.fa_bwd_offset.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64, _f32, _i64, _vp]
+    lib.fa_decode_split.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                    _i64, _i64, _f32, _vp]
+    lib.fa_decode_split_offset.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                           _i64, _i64, _i64, _f32, _i64, _vp]
+    lib.fa_merge_states.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                    _vp]
+    lib.fa_status_str.argtypes = [_int]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    for f in ("fa_fwd", "fa_fwd_offset", "fa_fwd_blocked", "fa_bwd", "fa_bwd_offset",
+              "fa_decode_split", "fa_decode_split_offset", "fa_merge_states"):
+        getattr(lib, f).restype = _int
+    return lib
+
+
+_lib = _declare(ctypes.CDLL(LIB_PATH))
 
 EXPORTS = ("fa_fwd", "fa_fwd_offset", "fa_fwd_blocked", "fa_bwd_workspace_size", "fa_bwd",
            "fa_bwd_offset", "fa_decode_split", "fa_decode_split_offset", "fa_merge_states",

@@ -1,7 +1,9 @@
 """Build libfa.so from csrc/*.hip with hipcc for gfx950 (in-tree, no JIT cache).
 
 Each source is compiled to an object in parallel, then linked into
-``flashattention_online_softmax_fa_amd/libfa.so``.  Run it as a script
+``flashattention_online_softmax_fa_amd/libfa.so``; the same sources compiled
+with FA_STATS=1 give the debug build ``libfa_stats.so``, whose kernels also
+count events (include/fa_stats.h).  Run it as a script
 (``python flashattention_online_softmax_fa_amd/build.py``) or through
 ``__graft_entry__.build()``; importing the package itself needs the built
 library.
@@ -19,6 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 SO = os.path.join(PKG, "libfa.so")
+STATS_SO = os.path.join(PKG, "libfa_stats.so")
 
 SOURCES = ["fa_api.hip", "fwd_f32.hip", "fwd_bf16.hip", "bwd.hip", "bwd_f32.hip", "decode.hip"]
 
@@ -43,9 +46,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; ROCm is required to build libfa.so")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-c",
+def _compile(job) -> str:
+    src, objdir, extra = job
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(x for x in (r.stderr or "").splitlines()
@@ -55,19 +59,31 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libfa.so; returns its path."""
-    os.makedirs(OBJDIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = SO + ".tmp"
+def _link(objs, so: str) -> None:
+    tmp = so + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, SO)
-    if verbose:
-        print(f"built {SO}")
+    os.replace(tmp, so)
+
+
+def build(verbose: bool = False, stats: bool = True) -> str:
+    """Compile every source and link libfa.so (and, with ``stats``, the debug
+    build libfa_stats.so); returns the path of libfa.so."""
+    variants = [(SO, OBJDIR, [])]
+    if stats:
+        variants.append((STATS_SO, os.path.join(OBJDIR, "stats"), ["-DFA_STATS=1"]))
+    jobs = []
+    for _, objdir, extra in variants:
+        os.makedirs(objdir, exist_ok=True)
+        jobs += [(src, objdir, extra) for src in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, jobs))
+    for k, (so, _, _) in enumerate(variants):
+        _link(objs[k * len(SOURCES):(k + 1) * len(SOURCES)], so)
+        if verbose:
+            print(f"built {so}")
     return SO
 
 

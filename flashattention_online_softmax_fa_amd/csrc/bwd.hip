@@ -38,6 +38,10 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 
+#if FA_STATS
+__device__ unsigned long long g_bwd_stats[kStatCount];
+#endif
+
 // Eight fp32 accumulator registers r0..r0+7 -> bf16x8 (round to nearest even).
 __device__ __forceinline__ bf16x8 pack8(const f32x16 &v, int r0) {
     const u32x4 w = {pack_bf16x2(v[r0 + 0], v[r0 + 1]), pack_bf16x2(v[r0 + 2], v[r0 + 3]),
@@ -189,6 +193,9 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
             dkacc[b][r] = 0.f;
         }
 
+#if FA_STATS
+    uint32_t st_tiles = 0;
+#endif
     // query tiles that can see this key tile (causal: query q sees keys
     // 0 .. q + qoff)
     const int nqt = (int)((Nq + BR - 1) / BR);
@@ -210,8 +217,12 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         lds_barrier();
         if (it + ST - 1 < nqt) issue(it + ST - 1, (idx + ST - 1) % ST);
         const int64_t q0 = (int64_t)it * BR;
-        const bool active = kw0 < Nk && (!CAUSAL || q0 + BR - 1 + qoff >= kw0);
+        const int64_t q_last = (q0 + BR < Nq ? q0 + BR : Nq) - 1;  // last real query of the tile
+        const bool active = kw0 < Nk && (!CAUSAL || q_last + qoff >= kw0);
         if (!active) continue;
+#if FA_STATS
+        ++st_tiles;
+#endif
         const uint8_t *qt = smem + (idx % ST) * T::STAGEB;
         const uint8_t *ot = qt + T::TILEB;
         const float *lt = (const float *)(ot + T::TILEB);
@@ -279,6 +290,9 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         }
     }
 
+#if FA_STATS
+    if (lane == 0 && kw0 < Nk) atomicAdd(&g_bwd_stats[3], (unsigned long long)st_tiles);
+#endif
     // ---- epilogue: dK = scale * dK_acc, dV = dV_acc (lane: key lr; register r:
     //      column 32b + 8*(r/4) + 4g + r%4)
     if (mykey < Nk) {
@@ -388,6 +402,9 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     for (int b = 0; b < D / 32; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
+#if FA_STATS
+    uint32_t st_tiles = 0;
+#endif
 
 #pragma unroll
     for (int t = 0; t < ST - 1; ++t)
@@ -403,6 +420,9 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
         const int64_t kv0 = j * BC;
         const bool active = qw0 < Nq && (!CAUSAL || kv0 <= qw_last + qoff);
         if (!active) continue;
+#if FA_STATS
+        ++st_tiles;
+#endif
         const uint8_t *kt = smem + (j % ST) * 2 * T::TILEB;
         const uint8_t *vt = kt + T::TILEB;
 
@@ -455,6 +475,9 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
         }
     }
 
+#if FA_STATS
+    if (lane == 0 && qw0 < Nq) atomicAdd(&g_bwd_stats[4], (unsigned long long)st_tiles);
+#endif
     // ---- epilogue: dQ = scale * acc (lane: query lr; register r: column
     //      32b + 8*(r/4) + 4g + r%4)
     if (qrow < Nq) {
@@ -502,6 +525,24 @@ hipError_t launch_main(const BwdArgs &a, float *L2, hipStream_t s) {
 }
 
 }  // namespace
+
+#if FA_STATS
+hipError_t stats_bwd(unsigned long long *host, bool reset) {
+    if (reset) {
+        static const unsigned long long zero[kStatCount] = {};
+        return hipMemcpyToSymbol(HIP_SYMBOL(g_bwd_stats), zero, sizeof(zero));
+    }
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_bwd_stats), kStatCount * sizeof(*host));
+}
+
+void bwd_bf16_tiles(int64_t d, int causal, int64_t *kv_rows, int64_t *kv_cols, int64_t *q_rows,
+                    int64_t *q_cols) {
+    *kv_rows = 32;
+    *kv_cols = d == 64 && causal ? FA_BWD_DKDV_BR64 : 32;
+    *q_rows = 32;
+    *q_cols = d == 64 ? FA_BWD_DQ_BC64 : 32;
+}
+#endif
 
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s) {
     const int64_t rows = a.B * a.H * a.Nq;

@@ -4,6 +4,7 @@
 #include <cstdint>
 
 #include "../../include/fa.h"
+#include "../../include/fa_stats.h"
 #include "fa_internal.h"
 
 namespace {
@@ -204,6 +205,41 @@ fa_status fa_merge_states(fa_dtype dt, const float *part_m, const float *part_l,
     fa::MergeArgs a{part_m, part_l, part_o, O, L, B * H * Nq, d, n_split, dt == FA_BF16};
     return hip_status(fa::launch_merge_states(a, (hipStream_t)stream));
 }
+
+#if FA_STATS
+fa_status fa_stats_reset(void) {
+    if (hipDeviceSynchronize() != hipSuccess) return FA_ERR_HIP;
+    if (fa::stats_fwd(nullptr, true) != hipSuccess || fa::stats_bwd(nullptr, true) != hipSuccess)
+        return FA_ERR_HIP;
+    return FA_OK;
+}
+
+fa_status fa_stats_read(uint64_t *out) {
+    if (out == nullptr) return FA_ERR_INVALID_ARG;
+    if (hipDeviceSynchronize() != hipSuccess) return FA_ERR_HIP;
+    unsigned long long f[fa::kStatCount], b[fa::kStatCount];
+    if (fa::stats_fwd(f, false) != hipSuccess || fa::stats_bwd(b, false) != hipSuccess)
+        return FA_ERR_HIP;
+    for (int i = 0; i < fa::kStatCount; ++i) out[i] = f[i] + b[i];
+    return FA_OK;
+}
+
+fa_status fa_stats_tile(int kind, fa_dtype dt, int64_t d, int causal, int64_t *rows,
+                        int64_t *cols) {
+    if (rows == nullptr || cols == nullptr || kind < 0 || kind > 2) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (dt != FA_BF16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+    if (kind == 0) {
+        fa::fwd_bf16_tile(d, rows, cols);
+    } else {
+        int64_t kr, kc, qr, qc;
+        fa::bwd_bf16_tiles(d, causal, &kr, &kc, &qr, &qc);
+        *rows = kind == 1 ? kr : qr;
+        *cols = kind == 1 ? kc : qc;
+    }
+    return FA_OK;
+}
+#endif
 
 const char *fa_status_str(fa_status s) {
     switch (s) {

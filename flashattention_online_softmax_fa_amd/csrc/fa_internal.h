@@ -48,6 +48,20 @@ struct MergeArgs {
     int out_bf16;
 };
 
+// Debug build (FA_STATS=1): event counters of the bf16 kernels, one array per
+// source file, indexed by fa_stat (include/fa_stats.h).
+#ifndef FA_STATS
+#define FA_STATS 0
+#endif
+constexpr int kStatCount = 8;
+#if FA_STATS
+hipError_t stats_fwd(unsigned long long *host, bool reset);  // copy out, or zero
+hipError_t stats_bwd(unsigned long long *host, bool reset);
+void fwd_bf16_tile(int64_t d, int64_t *rows, int64_t *cols);
+void bwd_bf16_tiles(int64_t d, int causal, int64_t *kv_rows, int64_t *kv_cols, int64_t *q_rows,
+                    int64_t *q_cols);
+#endif
+
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s);

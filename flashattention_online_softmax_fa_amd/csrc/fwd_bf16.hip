@@ -59,7 +59,11 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr float kMargin = 8.f;         // base-2 headroom before the reference max is raised
+constexpr float kMargin = 8.f;
+
+#if FA_STATS
+__device__ unsigned long long g_fwd_stats[kStatCount];
+#endif         // base-2 headroom before the reference max is raised
 
 // D: head dimension; QB: 32-query blocks per wave (each K / V^T fragment read
 // from LDS feeds QB matrix-core products); BC: keys per tile.
@@ -200,6 +204,9 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         }
     }
 
+#if FA_STATS
+    uint32_t st_resc = 0;  // rows of this lane (g == 0) whose accumulator was rescaled
+#endif
     f32x16 oacc[QB][D / 32];
     f32x16 sacc[QB][KB], snxt[QB][KB];  // scores of the current and the next tile
     // m: reference maximum; l0 + l1: this lane's half of the row sum, in two
@@ -300,6 +307,9 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
                 const bool grow = mj > m[qb] + kMargin;  // same in both lanes of the row
                 const float m_new = grow ? mj : m[qb];
                 const float alpha = fast_exp2(m[qb] - m_new);  // 0 on the first tile, else <= 1
+#if FA_STATS
+                if (grow && m[qb] > -INFINITY && g == 0 && qw0 + 32 * qb + lr < Nq) ++st_resc;
+#endif
                 l0[qb] *= alpha;
                 l1[qb] *= alpha;
 #pragma unroll
@@ -429,6 +439,20 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
             if (g == 0) L[bh * Nq + qrow] = (m[qb] + log2f(l_tot)) * kLn2;
         }
     }
+#if FA_STATS
+    {
+        int r = (int)st_resc;
+        for (int o = 32; o > 0; o >>= 1) r += __shfl_xor(r, o);
+        if (lane == 0) {
+            if (qw0 < Nq) {
+                const int nk_all = (int)((Nk + BC - 1) / BC);
+                atomicAdd(&g_fwd_stats[0], (unsigned long long)nkt_w);
+                atomicAdd(&g_fwd_stats[1], (unsigned long long)(nk_all - nkt_w));
+            }
+            atomicAdd(&g_fwd_stats[2], (unsigned long long)r);
+        }
+    }
+#endif
 }
 
 template <int D, int QB, int BC, int ST, bool CAUSAL>
@@ -453,6 +477,21 @@ constexpr int kQB64 = FA_FWD_QB64, kBC64 = FA_FWD_BC64, kST64 = FA_FWD_ST64;
 constexpr int kQB128 = FA_FWD_QB128, kBC128 = FA_FWD_BC128, kST128 = FA_FWD_ST128;
 
 }  // namespace
+
+#if FA_STATS
+hipError_t stats_fwd(unsigned long long *host, bool reset) {
+    if (reset) {
+        static const unsigned long long zero[kStatCount] = {};
+        return hipMemcpyToSymbol(HIP_SYMBOL(g_fwd_stats), zero, sizeof(zero));
+    }
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_fwd_stats), kStatCount * sizeof(*host));
+}
+
+void fwd_bf16_tile(int64_t d, int64_t *rows, int64_t *cols) {
+    *rows = d == 128 ? Tile<128, kQB128, kBC128, kST128>::QW : Tile<64, kQB64, kBC64, kST64>::QW;
+    *cols = d == 128 ? kBC128 : kBC64;
+}
+#endif
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s) {
     if (a.d == 128)

@@ -179,3 +179,41 @@ def test_merge_rejects(lib):
     assert call(O=NULL) == FA_ERR_INVALID_ARG
     assert call(O=P + 1) == FA_ERR_INVALID_ARG
     assert call(d=513) == FA_ERR_UNSUPPORTED
+
+
+STATS_SO = os.path.join(ROOT, "flashattention_online_softmax_fa_amd", "libfa_stats.so")
+STATS_HEADER = os.path.join(ROOT, "include", "fa_stats.h")
+
+
+def test_stats_build_exports():
+    """The debug build exports the release calls plus include/fa_stats.h's;
+    the release build exports none of the latter."""
+    text = re.sub(r"/\*.*?\*/", "", open(STATS_HEADER).read(), flags=re.S)
+    stats = sorted(set(re.findall(r"\b(fa_stats_[a-z_0-9]+)\s*\(", text)))
+    assert stats == ["fa_stats_read", "fa_stats_reset", "fa_stats_tile"]
+    dbg = ctypes.CDLL(STATS_SO)
+    for name in _declared() + stats:
+        assert hasattr(dbg, name), name
+    rel = ctypes.CDLL(SO)
+    for name in stats:
+        assert not hasattr(rel, name), name
+
+
+def test_stats_tile_shapes():
+    """fa_stats_tile is host-only: block shapes of the counted kernels."""
+    dbg = ctypes.CDLL(STATS_SO)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    dbg.fa_stats_tile.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int, i64p,
+                                  i64p]
+    r, c = ctypes.c_int64(), ctypes.c_int64()
+    for kind in (0, 1, 2):
+        for d in (64, 128):
+            for causal in (0, 1):
+                assert dbg.fa_stats_tile(kind, FA_BF16, d, causal, ctypes.byref(r),
+                                         ctypes.byref(c)) == FA_OK
+                assert r.value >= 32 and r.value % 32 == 0 and c.value % 32 == 0
+    assert dbg.fa_stats_tile(0, FA_F32, 64, 0, ctypes.byref(r), ctypes.byref(c)) == \
+        FA_ERR_UNSUPPORTED
+    assert dbg.fa_stats_tile(3, FA_BF16, 64, 0, ctypes.byref(r), ctypes.byref(c)) == \
+        FA_ERR_INVALID_ARG
+    assert dbg.fa_stats_tile(0, FA_BF16, 64, 0, None, ctypes.byref(c)) == FA_ERR_INVALID_ARG
