@@ -163,6 +163,29 @@ def roofline(run, ms, name):
             "kernel": run["kernel"], "launch_ms": round(ms, 5)}
 
 
+def io_model(run, fa_mod):
+    """HBM bytes of one forward call under the page's io_flash model
+    (flash_forward's IO count in attention_kernels.py: Q read once, O and L
+    written once, K and V read once per query tile, or once in total when they
+    stay in cache), in bytes for bf16 tensors and an fp32 L, next to the
+    measured traffic.  The query tile is the workgroup's rows (4 wavefronts)."""
+    cfg = run["cfg"]
+    B, H, Nq, Nk, d = cfg["B"], cfg["H"], cfg["Nq"], cfg["Nk"], cfg["d"]
+    rows = None
+    try:
+        from flashattention_online_softmax_fa_amd import stats
+        rows = 4 * stats.load().tile(0, d, cfg["causal"])[0]
+    except (ImportError, OSError):
+        pass
+    once = B * H * (2 * Nq * d * 2 + Nq * 4)         # Q read, O written, L written
+    kv = B * H * 2 * Nk * d * 2                      # K and V read once
+    out = {"kv_cached_bytes": float(once + kv), "query_tile_rows": rows,
+           "kv_per_query_tile_bytes": None}
+    if rows:
+        out["kv_per_query_tile_bytes"] = float(once + kv * math.ceil(Nq / rows))
+    return out
+
+
 def cpu_baseline(run, budget_s=12.0):
     """The fp64 oracle (dense definition) on a bounded sample of query rows of
     the same inputs, in the metric's unit."""
@@ -234,6 +257,8 @@ def main():
         "config": run["cfg"],
         "roofline": roofline(run, ms, args.workload),
     }
+    if run["kernel"] == "fwd_bf16_kernel":
+        line["roofline"]["io_flash"] = io_model(run, fa)
     if "partial_bytes" in run:
         line["config"]["partial_state_bytes"] = run["partial_bytes"][run["state"]["n"]]
     if "extra" in run:
@@ -254,6 +279,8 @@ def main():
             parts[name] = {"ms": round(pms, 5), "value": round(rate(r, pms), 3),
                            "unit": rf["unit"], "frac": rf["frac"], "traffic": rf["traffic"],
                            "config": r["cfg"]}
+            if r["kernel"] == "fwd_bf16_kernel":
+                parts[name]["io_flash"] = io_model(r, fa)
             if "partial_bytes" in r:
                 parts[name]["partial_state_bytes"] = r["partial_bytes"][r["state"]["n"]]
             del r
