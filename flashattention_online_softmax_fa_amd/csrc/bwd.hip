@@ -32,6 +32,8 @@
 #include "fa_device.h"
 #include "fa_internal.h"
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
@@ -193,6 +195,80 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
             dkacc[b][r] = 0.f;
         }
 
+    // One query tile against this wave's keys; MASKED instances handle the
+    // causal diagonal and the ragged ends, the rest carry no mask code.
+    auto tile = [&](const uint8_t *qt, int64_t q0, auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+        const uint8_t *ot = qt + T::TILEB;
+        const float *lt = (const float *)(ot + T::TILEB);
+        const float *dt = lt + T::VECB / 4;
+
+        // ---- S = Q K^T and dP = dO V^T (lane: key lr; register r: query
+        //      8*(r/4) + 4g + r%4 of the 32-query block)
+        f32x16 sacc[QB], pacc[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                sacc[qb][r] = 0.f;
+                pacc[qb][r] = 0.f;
+            }
+#pragma unroll
+            for (int ds = 0; ds < D / 16; ++ds) {
+                const int off = qb * 32 * ROWB + roff[ds];
+                const bf16x8 aq = *(const bf16x8 *)(qt + off);
+                const bf16x8 ao = *(const bf16x8 *)(ot + off);
+                sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ds], sacc[qb], 0, 0, 0);
+                pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[ds], pacc[qb], 0, 0, 0);
+            }
+        }
+        // ---- P = exp2(S c - L2), dS = P (dP - D); masked tiles zero the pairs
+        //      past Nq, past Nk, and (causal) where the key comes after the query:
+        //      query offset o in the tile is visible iff lo <= o <= hi
+        int lo = 0, hi = BR - 1;
+        if (MASKED) {
+            int64_t lo64 = CAUSAL ? mykey - qoff - q0 : 0;
+            int64_t hi64 = Nq - 1 - q0;
+            if (mykey >= Nk) hi64 = -1;
+            lo = (int)(lo64 < 0 ? 0 : (lo64 > BR ? BR : lo64));
+            hi = (int)(hi64 > BR - 1 ? BR - 1 : (hi64 < -1 ? -1 : hi64));
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int qi = qb * 32 + 8 * r4 + 4 * g;
+                const f32x4 lv = *(const f32x4 *)(lt + qi);
+                const f32x4 dv = *(const f32x4 *)(dt + qi);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * r4 + e;
+                    float p = fast_exp2(fmaf(sacc[qb][r], c, -lv[e]));
+                    if (MASKED && (qi + e < lo || qi + e > hi)) p = 0.f;
+                    sacc[qb][r] = p;
+                    pacc[qb][r] = p * (pacc[qb][r] - dv[e]);
+                }
+            }
+        }
+        // ---- dV^T += dO^T P and dK^T += Q^T dS.  B operand (k-step kq of 16
+        //      queries) = registers 8h..8h+7 of block kq/2, so k-slot (g, e) is
+        //      query 8*(e/4) + 4g + e%4 of the step; the transposed A operand is
+        //      read in the same slot order.
+#pragma unroll
+        for (int kq = 0; kq < BR / 16; ++kq) {
+            const bf16x8 pb = pack8(sacc[kq >> 1], 8 * (kq & 1));
+            const bf16x8 sb = pack8(pacc[kq >> 1], 8 * (kq & 1));
+#pragma unroll
+            for (int b = 0; b < D / 32; ++b) {
+                const int off = kq * 16 * ROWB;
+                const bf16x8 ao = tr_pair<ROWB>(ot + off, toff[b]);
+                const bf16x8 aq = tr_pair<ROWB>(qt + off, toff[b]);
+                dvacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb, dvacc[b], 0, 0, 0);
+                dkacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb, dkacc[b], 0, 0, 0);
+            }
+        }
+    };
+
 #if FA_STATS
     uint32_t st_tiles = 0;
 #endif
@@ -224,70 +300,13 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         ++st_tiles;
 #endif
         const uint8_t *qt = smem + (idx % ST) * T::STAGEB;
-        const uint8_t *ot = qt + T::TILEB;
-        const float *lt = (const float *)(ot + T::TILEB);
-        const float *dt = lt + T::VECB / 4;
-
-        // ---- S = Q K^T and dP = dO V^T (lane: key lr; register r: query
-        //      8*(r/4) + 4g + r%4 of the 32-query block)
-        f32x16 sacc[QB], pacc[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                sacc[qb][r] = 0.f;
-                pacc[qb][r] = 0.f;
-            }
-#pragma unroll
-            for (int ds = 0; ds < D / 16; ++ds) {
-                const int off = qb * 32 * ROWB + roff[ds];
-                const bf16x8 aq = *(const bf16x8 *)(qt + off);
-                const bf16x8 ao = *(const bf16x8 *)(ot + off);
-                sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ds], sacc[qb], 0, 0, 0);
-                pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[ds], pacc[qb], 0, 0, 0);
-            }
-        }
-        // ---- P = exp2(S c - L2), dS = P (dP - D); zero past Nq, past Nk, and
-        //      (causal) where the key comes after the query
+        // the mask is needed on the causal diagonal and at the ragged ends only
         const bool need_mask =
             (q0 + BR > Nq) || (kw0 + 32 > Nk) || (CAUSAL && q0 + qoff < kw0 + 31);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int qi = qb * 32 + 8 * r4 + 4 * g;
-                const f32x4 lv = *(const f32x4 *)(lt + qi);
-                const f32x4 dv = *(const f32x4 *)(dt + qi);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * r4 + e;
-                    float p = fast_exp2(fmaf(sacc[qb][r], c, -lv[e]));
-                    if (need_mask) {
-                        const int64_t q = q0 + qi + e;
-                        if (q >= Nq || mykey >= Nk || (CAUSAL && mykey > q + qoff)) p = 0.f;
-                    }
-                    sacc[qb][r] = p;
-                    pacc[qb][r] = p * (pacc[qb][r] - dv[e]);
-                }
-            }
-        }
-        // ---- dV^T += dO^T P and dK^T += Q^T dS.  B operand (k-step kq of 16
-        //      queries) = registers 8h..8h+7 of block kq/2, so k-slot (g, e) is
-        //      query 8*(e/4) + 4g + e%4 of the step; the transposed A operand is
-        //      read in the same slot order.
-#pragma unroll
-        for (int kq = 0; kq < BR / 16; ++kq) {
-            const bf16x8 pb = pack8(sacc[kq >> 1], 8 * (kq & 1));
-            const bf16x8 sb = pack8(pacc[kq >> 1], 8 * (kq & 1));
-#pragma unroll
-            for (int b = 0; b < D / 32; ++b) {
-                const int off = kq * 16 * ROWB;
-                const bf16x8 ao = tr_pair<ROWB>(ot + off, toff[b]);
-                const bf16x8 aq = tr_pair<ROWB>(qt + off, toff[b]);
-                dvacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb, dvacc[b], 0, 0, 0);
-                dkacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb, dkacc[b], 0, 0, 0);
-            }
-        }
+        if (need_mask)
+            tile(qt, q0, std::true_type{});
+        else
+            tile(qt, q0, std::false_type{});
     }
 
 #if FA_STATS
@@ -406,24 +425,15 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     uint32_t st_tiles = 0;
 #endif
 
-#pragma unroll
-    for (int t = 0; t < ST - 1; ++t)
-        if (t < nkt) issue(t, t);
-
-    for (int64_t j = 0; j < nkt; ++j) {
-        if (ST == 3 && j + 1 < nkt)
-            wait_vm<(ST == 3 ? 2 * T::IPW : 0)>();
-        else
-            wait_vm<0>();
-        lds_barrier();
-        if (j + ST - 1 < nkt) issue(j + ST - 1, (int)((j + ST - 1) % ST));
+    // One key tile against this wave's queries; MASKED instances handle the
+    // causal diagonal and the ragged end, the rest carry no mask code.
+    auto tile = [&](int64_t j, auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
         const int64_t kv0 = j * BC;
-        const bool active = qw0 < Nq && (!CAUSAL || kv0 <= qw_last + qoff);
-        if (!active) continue;
+        const uint8_t *kt = smem + (j % ST) * 2 * T::TILEB;
 #if FA_STATS
         ++st_tiles;
 #endif
-        const uint8_t *kt = smem + (j % ST) * 2 * T::TILEB;
         const uint8_t *vt = kt + T::TILEB;
 
         // ---- S^T = K Q^T, dP^T = V dO^T (lane: query lr; register r: key
@@ -445,10 +455,10 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
                 pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[ds], pacc[kb], 0, 0, 0);
             }
         }
-        // ---- P = exp2(S c - L2), dS = P (dP - D), both per lane
-        const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > qw0 + qoff);
+        // ---- P = exp2(S c - L2), dS = P (dP - D), both per lane; masked tiles
+        //      zero the keys past Nk and after the query
         int lim = BC;
-        if (need_mask) {
+        if (MASKED) {
             int64_t lim64 = Nk - 1 - kv0;  // last visible key offset
             if (CAUSAL && qrow + qoff - kv0 < lim64) lim64 = qrow + qoff - kv0;
             lim = (int)(lim64 < -1 ? -1 : (lim64 > BC ? BC : lim64)) - 4 * g;
@@ -458,7 +468,7 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float p = fast_exp2(fmaf(sacc[kb][r], c, -l2));
-                if (need_mask && kb * 32 + 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
+                if (MASKED && kb * 32 + 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
                 pacc[kb][r] = p * (pacc[kb][r] - dq);
             }
         // ---- dQ^T += K^T dS^T.  B operand (k-step ks of 16 keys) = registers
@@ -473,6 +483,37 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
                 acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, acc[b], 0, 0, 0);
             }
         }
+    };
+    // ring step j: tile j has landed and is visible to every wave; the slot
+    // read in step j-1 is refilled
+    auto ring = [&](int64_t j) {
+        if (ST == 3 && j + 1 < nkt)
+            wait_vm<(ST == 3 ? 2 * T::IPW : 0)>();
+        else
+            wait_vm<0>();
+        lds_barrier();
+        if (j + ST - 1 < nkt) issue(j + ST - 1, (int)((j + ST - 1) % ST));
+    };
+    // leading tiles with every key visible to every query of this wave
+    int64_t nfull = 0;
+    if (qw0 < Nq) {
+        nfull = Nk / BC;
+        if (CAUSAL && (qw0 + qoff + 1) / BC < nfull) nfull = (qw0 + qoff + 1) / BC;
+        if (nfull > nkt) nfull = nkt;
+    }
+
+#pragma unroll
+    for (int t = 0; t < ST - 1; ++t)
+        if (t < nkt) issue(t, t);
+    int64_t j = 0;
+    for (; j < nfull; ++j) {
+        ring(j);
+        tile(j, std::false_type{});
+    }
+    for (; j < nkt; ++j) {
+        ring(j);
+        const bool active = qw0 < Nq && (!CAUSAL || j * BC <= qw_last + qoff);
+        if (active) tile(j, std::true_type{});
     }
 
 #if FA_STATS
