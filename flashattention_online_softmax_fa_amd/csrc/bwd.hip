@@ -131,7 +131,8 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     constexpr int QB = T::QB, ROWB = T::ROWB;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * T::STAGEB];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = tid >> 6;
     const int g = lane >> 5, lr = lane & 31;
     const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = lid / nkt;
@@ -153,25 +154,37 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     }
 
     // ring loads: this lane fills chunk `lane` of its IPW 1 KiB blocks of the
-    // Q and dO tiles; waves 0 and 1 also fill the L2 and D slices
-    int ld_row[T::IPW], ld_col[T::IPW];
+    // Q and dO tiles (row (wave*IPW + u)*RPI + lane/CH of the tile, logical
+    // chunk (lane % CH) ^ swz(row)); waves 0 and 1 also fill the L2 and D slices
+    auto ld_row = [&](int u) { return (wave * T::IPW + u) * T::RPI + lane / T::CH; };
+    uint32_t ld_off[T::IPW];  // byte offset of this lane's load within a tile
 #pragma unroll
-    for (int u = 0; u < T::IPW; ++u) {
-        const int row = (wave * T::IPW + u) * T::RPI + lane / T::CH;
-        ld_row[u] = row;
-        ld_col[u] = (lane % T::CH) ^ swz<ROWB>(row);
-    }
+    for (int u = 0; u < T::IPW; ++u) ld_off[u] = (uint32_t)chunk_off<ROWB>(ld_row(u), lane % T::CH);
     auto issue = [&](int it, int st) {
         const int64_t q0 = (int64_t)it * BR;
         uint8_t *qb = smem + st * T::STAGEB;
         uint8_t *ob = qb + T::TILEB;
+        if (q0 + 64 <= Nq) {  // every row and vector lane below in range: scalar bases
+            const uint8_t *qs = (const uint8_t *)(Qh + q0 * D);
+            const uint8_t *os = (const uint8_t *)(dOh + q0 * D);
+#pragma unroll
+            for (int u = 0; u < T::IPW; ++u) {
+                const int blk = wave * T::IPW + u;
+                dma16_s(qs, ld_off[u], qb + blk * 1024);
+                dma16_s(os, ld_off[u], ob + blk * 1024);
+            }
+            if (wave < 2) dma4((wave == 0 ? L2h : Dh) + q0 + lane, ob + T::TILEB + wave * T::VECB);
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < T::IPW; ++u) {
-            int64_t q = q0 + ld_row[u];
-            q = q < Nq ? q : Nq - 1;  // past the end: a real row, masked in compute
+            const int row = ld_row(u);
+            const int64_t q = q0 + row < Nq ? q0 + row : Nq - 1;  // past the end: masked later
+            const uint8_t *src = (const uint8_t *)(Qh + q * D) + (ld_off[u] - row * ROWB);
+            const uint8_t *srco = (const uint8_t *)(dOh + q * D) + (ld_off[u] - row * ROWB);
             const int blk = wave * T::IPW + u;
-            dma16(Qh + q * D + ld_col[u] * 8, qb + blk * 1024);
-            dma16(dOh + q * D + ld_col[u] * 8, ob + blk * 1024);
+            dma16(src, qb + blk * 1024);
+            dma16(srco, ob + blk * 1024);
         }
         if (wave < 2) {
             int64_t q = q0 + lane;
@@ -359,7 +372,8 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     constexpr int ROWB = T::ROWB;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * 2 * T::TILEB];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, lr = lane & 31;
     const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = lid / nqt;
@@ -390,24 +404,33 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     const float l2 = qrow < Nq ? L2[bh * Nq + qc] : INFINITY;  // padded row: P = 0
     const float dq = qrow < Nq ? Dv[bh * Nq + qc] : 0.f;
 
-    int ld_row[T::IPW], ld_col[T::IPW];
+    auto ld_row = [&](int u) { return (wave * T::IPW + u) * T::RPI + lane / T::CH; };
+    uint32_t ld_off[T::IPW];  // byte offset of this lane's load within a tile
 #pragma unroll
-    for (int u = 0; u < T::IPW; ++u) {
-        const int row = (wave * T::IPW + u) * T::RPI + lane / T::CH;
-        ld_row[u] = row;
-        ld_col[u] = (lane % T::CH) ^ swz<ROWB>(row);
-    }
+    for (int u = 0; u < T::IPW; ++u) ld_off[u] = (uint32_t)chunk_off<ROWB>(ld_row(u), lane % T::CH);
     auto issue = [&](int64_t j, int st) {
         const int64_t kv0 = j * BC;
         uint8_t *kb = smem + st * 2 * T::TILEB;
         uint8_t *vb = kb + T::TILEB;
+        if (kv0 + BC <= Nk) {  // whole tile in range: scalar bases
+            const uint8_t *ks = (const uint8_t *)(Kh + kv0 * D);
+            const uint8_t *vs = (const uint8_t *)(Vh + kv0 * D);
+#pragma unroll
+            for (int u = 0; u < T::IPW; ++u) {
+                const int blk = wave * T::IPW + u;
+                dma16_s(ks, ld_off[u], kb + blk * 1024);
+                dma16_s(vs, ld_off[u], vb + blk * 1024);
+            }
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < T::IPW; ++u) {
-            int64_t key = kv0 + ld_row[u];
-            key = key < Nk ? key : Nk - 1;  // past the end: a real row, masked later
+            const int row = ld_row(u);
+            const int64_t key = kv0 + row < Nk ? kv0 + row : Nk - 1;  // past the end: masked
+            const uint32_t col = ld_off[u] - row * ROWB;
             const int blk = wave * T::IPW + u;
-            dma16(Kh + key * D + ld_col[u] * 8, kb + blk * 1024);
-            dma16(Vh + key * D + ld_col[u] * 8, vb + blk * 1024);
+            dma16((const uint8_t *)(Kh + key * D) + col, kb + blk * 1024);
+            dma16((const uint8_t *)(Vh + key * D) + col, vb + blk * 1024);
         }
     };
     int koff[D / 16], toff[D / 32];

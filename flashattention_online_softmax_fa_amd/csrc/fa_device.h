@@ -133,6 +133,13 @@ __device__ __forceinline__ void dma16(const void *src, uint8_t *dst) {
                      :: "v"(src), "s"(lds_addr(dst)) : "memory");
 }
 
+// The same with a wave-uniform base address (scalar registers) and a 32-bit
+// per-lane byte offset: no vector address arithmetic per load.
+__device__ __forceinline__ void dma16_s(const void *base, uint32_t off, uint8_t *dst) {
+    __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                     :: "v"(off), "s"(base), "s"(lds_addr(dst)) : "memory");
+}
+
 // 4-byte DMA: lane i of the wave writes dst + 4*i.
 __device__ __forceinline__ void dma4(const void *src, uint8_t *dst) {
     __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"

@@ -160,8 +160,8 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         if (kv0 + BC <= Nk) {
 #pragma unroll
             for (int u = 0; u < T::IPW; ++u) {
-                dma16(kt + ld_off[u], kb + u * 1024);
-                dma16(vt + ld_off[u], vb + u * 1024);
+                dma16_s(kt, (uint32_t)ld_off[u], kb + u * 1024);
+                dma16_s(vt, (uint32_t)ld_off[u], vb + u * 1024);
             }
         } else {  // rows past Nk re-read the last key; they are masked
 #pragma unroll
