@@ -101,6 +101,20 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
+// Wait until at most n (0 <= n <= MAX, wave-uniform) groups of PER loads of
+// this wave are still in flight.
+template <int PER, int MAX>
+__device__ __forceinline__ void wait_steps(int n) {
+    if constexpr (MAX == 0) {
+        wait_vm<0>();
+    } else {
+        if (n >= MAX)
+            wait_vm<MAX * PER>();
+        else
+            wait_steps<PER, MAX - 1>(n);
+    }
+}
+
 // Workgroup barrier that orders LDS accesses but does not drain outstanding
 // global loads (a ring prefetch stays in flight across it).
 __device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
@@ -135,9 +149,15 @@ __device__ __forceinline__ void dma16(const void *src, uint8_t *dst) {
 
 // The same with a wave-uniform base address (scalar registers) and a 32-bit
 // per-lane byte offset: no vector address arithmetic per load.
+// `base` must be the same in every lane; it is read from the first lane.
 __device__ __forceinline__ void dma16_s(const void *base, uint32_t off, uint8_t *dst) {
+    // readfirstlane returns int: widen through uint32_t, never by sign extension
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint64_t u = ((uint64_t)hi << 32) | (uint64_t)lo;
     __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                     :: "v"(off), "s"(base), "s"(lds_addr(dst)) : "memory");
+                     :: "v"(off), "s"((const void *)(uintptr_t)u), "s"(lds_addr(dst)) : "memory");
 }
 
 // 4-byte DMA: lane i of the wave writes dst + 4*i.

@@ -83,20 +83,6 @@ struct Tile {
     static_assert(BC % 32 == 0, "32-key blocks");
 };
 
-// Wait until at most n (0 <= n <= MAX, wave-uniform) groups of PER loads of
-// this wave are still in flight.
-template <int PER, int MAX>
-__device__ __forceinline__ void wait_steps(int n) {
-    if constexpr (MAX == 0) {
-        wait_vm<0>();
-    } else {
-        if (n >= MAX)
-            wait_vm<MAX * PER>();
-        else
-            wait_steps<PER, MAX - 1>(n);
-    }
-}
-
 template <int D, int QB, int BC, int ST, bool CAUSAL, bool POS_SCALE>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D * QB >= 256 ? 1 : (D == 64 ? FA_FWD_W64 : FA_FWD_W128), 4)))
