@@ -134,9 +134,9 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = tid >> 6;
     const int g = lane >> 5, lr = lane & 31;
-    const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int64_t bh = lid / nkt;
-    const int kt = (int)(lid % nkt);  // causal: low key tiles see the most queries; go first
+    const TileId tid_ = tile_order(blockIdx.x, gridDim.x / (uint32_t)nkt, (uint32_t)nkt);
+    const int64_t bh = tid_.head;
+    const int kt = (int)tid_.rank;  // causal: early keys are seen by the most queries
     const int64_t k0 = (int64_t)kt * T::KEYS;
     const int64_t kw0 = k0 + wave * 32;
     const int64_t mykey = kw0 + lr;
@@ -160,20 +160,24 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     uint32_t ld_off[T::IPW];  // byte offset of this lane's load within a tile
 #pragma unroll
     for (int u = 0; u < T::IPW; ++u) ld_off[u] = (uint32_t)chunk_off<ROWB>(ld_row(u), lane % T::CH);
+    // LDS destinations as scalar byte addresses: this wave's first block in
+    // stage 0, and its L2 / D slice (waves 0 and 1)
+    const uint32_t wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t lds_w = lds_addr(smem) + wave_u * (T::IPW * 1024);
+    const uint32_t lds_v = lds_addr(smem) + 2 * T::TILEB + wave_u * T::VECB;
     auto issue = [&](int it, int st) {
         const int64_t q0 = (int64_t)it * BR;
-        uint8_t *qb = smem + st * T::STAGEB;
-        uint8_t *ob = qb + T::TILEB;
+        const uint32_t qb = lds_w + st * T::STAGEB, ob = qb + T::TILEB;
+        const uint32_t vb = lds_v + st * T::STAGEB;
         if (q0 + 64 <= Nq) {  // every row and vector lane below in range: scalar bases
             const uint8_t *qs = (const uint8_t *)(Qh + q0 * D);
             const uint8_t *os = (const uint8_t *)(dOh + q0 * D);
 #pragma unroll
             for (int u = 0; u < T::IPW; ++u) {
-                const int blk = wave * T::IPW + u;
-                dma16_s(qs, ld_off[u], qb + blk * 1024);
-                dma16_s(os, ld_off[u], ob + blk * 1024);
+                dma16_s(qs, ld_off[u], qb + u * 1024);
+                dma16_s(os, ld_off[u], ob + u * 1024);
             }
-            if (wave < 2) dma4((wave == 0 ? L2h : Dh) + q0 + lane, ob + T::TILEB + wave * T::VECB);
+            if (wave_u < 2) dma4((wave_u == 0 ? L2h : Dh) + q0 + lane, vb);
             return;
         }
 #pragma unroll
@@ -182,14 +186,13 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
             const int64_t q = q0 + row < Nq ? q0 + row : Nq - 1;  // past the end: masked later
             const uint8_t *src = (const uint8_t *)(Qh + q * D) + (ld_off[u] - row * ROWB);
             const uint8_t *srco = (const uint8_t *)(dOh + q * D) + (ld_off[u] - row * ROWB);
-            const int blk = wave * T::IPW + u;
-            dma16(src, qb + blk * 1024);
-            dma16(srco, ob + blk * 1024);
+            dma16(src, qb + u * 1024);
+            dma16(srco, ob + u * 1024);
         }
-        if (wave < 2) {
+        if (wave_u < 2) {
             int64_t q = q0 + lane;
             q = q < Nq ? q : Nq - 1;
-            dma4((wave == 0 ? L2h : Dh) + q, ob + T::TILEB + wave * T::VECB);
+            dma4((wave_u == 0 ? L2h : Dh) + q, vb);
         }
     };
 
@@ -375,10 +378,9 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, lr = lane & 31;
-    const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int64_t bh = lid / nqt;
-    int qt = (int)(lid % nqt);
-    if (CAUSAL) qt = nqt - 1 - qt;  // heaviest query tiles first
+    const TileId tid_ = tile_order(blockIdx.x, gridDim.x / (uint32_t)nqt, (uint32_t)nqt);
+    const int64_t bh = tid_.head;
+    const int qt = CAUSAL ? nqt - 1 - (int)tid_.rank : (int)tid_.rank;  // causal: late queries see the most keys
     const int64_t q0 = (int64_t)qt * T::BR;
     const int64_t qw0 = q0 + wave * 32;
     const int64_t qrow = qw0 + lr;

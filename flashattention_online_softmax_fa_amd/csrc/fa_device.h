@@ -141,37 +141,68 @@ __device__ __forceinline__ uint32_t lds_addr(uint8_t *p) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_u8 *)p);
 }
 
-// 16-byte DMA of `src` into LDS: lane i of the wave writes dst + 16*i.
-__device__ __forceinline__ void dma16(const void *src, uint8_t *dst) {
+// The DMA loads below take the LDS destination as a byte address in the LDS
+// aperture (lds_addr of a pointer, or lds_addr(smem) plus a wave-uniform byte
+// offset, which keeps the address arithmetic on the scalar unit).
+
+// 16-byte DMA of `src` into LDS: lane i of the wave writes lds + 16*i.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
     __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                     :: "v"(src), "s"(lds_addr(dst)) : "memory");
+                     :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
+__device__ __forceinline__ void dma16(const void *src, uint8_t *dst) { dma16(src, lds_addr(dst)); }
 
 // The same with a wave-uniform base address (scalar registers) and a 32-bit
 // per-lane byte offset: no vector address arithmetic per load.
 // `base` must be the same in every lane; it is read from the first lane.
-__device__ __forceinline__ void dma16_s(const void *base, uint32_t off, uint8_t *dst) {
+__device__ __forceinline__ void dma16_s(const void *base, uint32_t off, uint32_t lds) {
     // readfirstlane returns int: widen through uint32_t, never by sign extension
     const uint64_t a = (uint64_t)(uintptr_t)base;
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint64_t u = ((uint64_t)hi << 32) | (uint64_t)lo;
     __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                     :: "v"(off), "s"((const void *)(uintptr_t)u), "s"(lds_addr(dst)) : "memory");
+                     :: "v"(off), "s"((const void *)(uintptr_t)u),
+                        "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+__device__ __forceinline__ void dma16_s(const void *base, uint32_t off, uint8_t *dst) {
+    dma16_s(base, off, lds_addr(dst));
 }
 
-// 4-byte DMA: lane i of the wave writes dst + 4*i.
-__device__ __forceinline__ void dma4(const void *src, uint8_t *dst) {
+// 4-byte DMA: lane i of the wave writes lds + 4*i.
+__device__ __forceinline__ void dma4(const void *src, uint32_t lds) {
     __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-                     :: "v"(src), "s"(lds_addr(dst)) : "memory");
+                     :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
+__device__ __forceinline__ void dma4(const void *src, uint8_t *dst) { dma4(src, lds_addr(dst)); }
 
-// Workgroups are dealt round-robin over the 8 XCDs (bid % 8).  Give each XCD
-// a contiguous range of logical tiles so that tiles sharing K/V (one head)
-// share that XCD's L2.  Identity when the grid is not a multiple of 8.
-__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
-    if (nblocks % 8u) return bid;
-    return (bid % 8u) * (nblocks / 8u) + bid / 8u;
+// Workgroups are dealt round-robin over the 8 XCDs (bid % 8).  Workgroup
+// `bid` of a grid of heads * tiles -> (head, tile rank), rank 0 = the tile
+// with the most work.  When the heads split evenly over the XCDs, each XCD
+// takes a contiguous group of heads, so that the tiles sharing a head's
+// operands share that XCD's L2; inside the group (or over all heads when they
+// do not split evenly) the order is rank-major, so the heaviest tiles of every
+// head start first and the light ones fill the end of the launch.  (Head-major
+// order would leave one slot per CU running a head's heavy tiles while the
+// other has finished: about a third of a causal launch idle at the end.)
+#ifndef FA_TILE_MAJOR
+#define FA_TILE_MAJOR 1
+#endif
+struct TileId {
+    uint32_t head, rank;
+};
+__device__ __forceinline__ TileId tile_order(uint32_t bid, uint32_t heads, uint32_t tiles) {
+#if FA_TILE_MAJOR
+    if (heads % 8u == 0) {
+        const uint32_t G = heads / 8u, r = bid / 8u;
+        return {(bid % 8u) * G + r % G, r / G};
+    }
+    return {bid % heads, bid / heads};
+#else
+    const uint32_t nblocks = heads * tiles;
+    const uint32_t lid = nblocks % 8u ? bid : (bid % 8u) * (nblocks / 8u) + bid / 8u;
+    return {lid / tiles, lid % tiles};
+#endif
 }
 
 }  // namespace fa

@@ -99,10 +99,9 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, lr = lane & 31, s16 = lane & 15, G = lane >> 4;
     const int xaddr = (lane ^ 32) << 2;  // ds_bpermute address of the other half of the row
-    const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int64_t bh = lid / nqt;
-    int qt = (int)(lid % nqt);
-    if (CAUSAL) qt = nqt - 1 - qt;  // heaviest query tiles first
+    const TileId tid_ = tile_order(blockIdx.x, gridDim.x / (uint32_t)nqt, (uint32_t)nqt);
+    const int64_t bh = tid_.head;
+    const int qt = CAUSAL ? nqt - 1 - (int)tid_.rank : (int)tid_.rank;  // causal: late queries see the most keys
     const int64_t q0 = (int64_t)qt * T::BR;
     const int64_t qw0 = q0 + wave * T::QW;  // query block qb of this wave: qw0 + 32qb + lane%32
     const uint16_t *Kh = K + bh * Nk * D;
