@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--settle", type=float, default=0.3,
+                   help="keep warming up (untimed) until this many seconds have passed")
     p.add_argument("--workload", default="prefill_d64",
                    choices=["prefill_d64", "prefill_causal_d128", "bwd_causal_d64",
                             "decode_d128"])
@@ -111,10 +113,19 @@ def setup(name, fa, torch, n_split=None):
                 partial_bytes={n: 4.0 * B * H * Nq * n * (d + 2) * 2 for n in splits})
 
 
-def timed(torch, step, steps, warmup):
+def timed(torch, step, steps, warmup, settle_s):
+    """ms per step over exactly `steps` timed steps, after `warmup` untimed
+    steps and then more untimed steps until `settle_s` seconds of warm-up have
+    passed: the GPU clock climbs over the first tens of milliseconds of load,
+    and a short warm-up would time the climb instead of the steady state."""
+    t0 = time.perf_counter()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
@@ -126,19 +137,19 @@ def timed(torch, step, steps, warmup):
     return a.elapsed_time(b) / steps  # ms per step
 
 
-def measure(run, torch, steps, warmup):
+def measure(run, torch, steps, warmup, settle_s):
     """Time one workload; for decode pick the fastest split count."""
     if "splits" in run:
         best = None
         for n in run["splits"]:
             run["state"]["n"] = n
-            ms = timed(torch, run["step"], steps, warmup)
+            ms = timed(torch, run["step"], steps, warmup, settle_s)
             if best is None or ms < best[0]:
                 best = (ms, n)
         run["state"]["n"] = best[1]
         run["cfg"]["n_split"] = best[1]
         return best[0]
-    return timed(torch, run["step"], steps, warmup)
+    return timed(torch, run["step"], steps, warmup, settle_s)
 
 
 def rate(run, ms):
@@ -245,13 +256,13 @@ def main():
         copy_calibration(torch)
         return
     run = setup(args.workload, fa, torch, args.n_split)
-    ms = measure(run, torch, args.steps, args.warmup)
+    ms = measure(run, torch, args.steps, args.warmup, args.settle)
     value = rate(run, ms)
     line = {
         "metric": "attention TFLOP/s and % of bf16 MFMA peak (fwd/bwd); decode GB/s % HBM peak",
         "value": round(value, 3),
         "unit": run["unit"] if run["unit"] == "TFLOP/s" else "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "warmup_settle_s": args.settle,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": run["cfg"],
@@ -274,7 +285,7 @@ def main():
                 continue
             r = setup(name, fa, torch)
             steps = max(3, args.steps // 2) if name == "decode_d128" else args.steps
-            pms = measure(r, torch, steps, min(args.warmup, 3))
+            pms = measure(r, torch, steps, min(args.warmup, 3), args.settle)
             rf = roofline(r, pms, name)
             parts[name] = {"ms": round(pms, 5), "value": round(rate(r, pms), 3),
                            "unit": rf["unit"], "frac": rf["frac"], "traffic": rf["traffic"],

@@ -105,11 +105,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
 // ---------------------------------------------------------------------------
 // dK, dV: key-major.
 // ---------------------------------------------------------------------------
-template <int D, int BR_, int ST_>
+template <int D, int BR_, int ST_, int KB_>
 struct DkdvCfg {
     static constexpr int BR = BR_;                 // queries per tile
     static constexpr int QB = BR / 32;             // 32-query blocks per tile
-    static constexpr int KEYS = 32 * kWaves;       // keys per workgroup
+    static constexpr int KB = KB_;                 // 32-key blocks per wave
+    static constexpr int KEYS = 32 * KB * kWaves;  // keys per workgroup
     static constexpr int CH = D / 8, ROWB = D * 2;
     static constexpr int TILEB = BR * ROWB;        // one Q or dO tile
     static constexpr int VECB = 256;               // one L2 or D slice (64 lanes x 4 B)
@@ -120,14 +121,15 @@ struct DkdvCfg {
     static_assert(IPW >= 1 && BR <= 64 && ST >= 2 && ST <= 3, "dkdv tile");
 };
 
-template <int D, int BR, int ST, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, 2)))
+template <int D, int BR, int ST, int KB, bool CAUSAL>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(D == 64 && KB == 1 ? 2 : 1, KB == 1 ? 2 : 1)))
 void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                      const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
                      const float *__restrict__ L2, const float *__restrict__ Dv,
                      uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int64_t Nq, int64_t Nk,
                      int64_t qoff, int nkt, float scale, float c) {
-    using T = DkdvCfg<D, BR, ST>;
+    using T = DkdvCfg<D, BR, ST, KB>;
     constexpr int QB = T::QB, ROWB = T::ROWB;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * T::STAGEB];
 
@@ -138,20 +140,23 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     const int64_t bh = tid_.head;
     const int kt = (int)tid_.rank;  // causal: early keys are seen by the most queries
     const int64_t k0 = (int64_t)kt * T::KEYS;
-    const int64_t kw0 = k0 + wave * 32;
-    const int64_t mykey = kw0 + lr;
+    const int64_t kw0 = k0 + wave * 32 * KB;  // key block kb of this wave: kw0 + 32kb + lane%32
+    constexpr int KW = 32 * KB;                // keys per wave
     const uint16_t *Qh = Q + bh * Nq * D;
     const uint16_t *dOh = dO + bh * Nq * D;
     const float *L2h = L2 + bh * Nq;
     const float *Dh = Dv + bh * Nq;
 
     // K and V of this wave's keys: B operands of S = Q K^T and dP = dO V^T
-    bf16x8 kf[D / 16], vf[D / 16];
+    bf16x8 kf[KB][D / 16], vf[KB][D / 16];
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-        kf[ds] = __builtin_bit_cast(bf16x8, load_row16(K + bh * Nk * D, mykey, Nk, D, ds * 2 + g));
-        vf[ds] = __builtin_bit_cast(bf16x8, load_row16(V + bh * Nk * D, mykey, Nk, D, ds * 2 + g));
-    }
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) {
+            const int64_t key = kw0 + 32 * kb + lr;
+            kf[kb][ds] = __builtin_bit_cast(bf16x8, load_row16(K + bh * Nk * D, key, Nk, D, ds * 2 + g));
+            vf[kb][ds] = __builtin_bit_cast(bf16x8, load_row16(V + bh * Nk * D, key, Nk, D, ds * 2 + g));
+        }
 
     // ring loads: this lane fills chunk `lane` of its IPW 1 KiB blocks of the
     // Q and dO tiles (row (wave*IPW + u)*RPI + lane/CH of the tile, logical
@@ -202,14 +207,16 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
 #pragma unroll
     for (int b = 0; b < D / 32; ++b) toff[b] = tr_off<ROWB>(lane, b, 0);
 
-    f32x16 dvacc[D / 32], dkacc[D / 32];
+    f32x16 dvacc[KB][D / 32], dkacc[KB][D / 32];
 #pragma unroll
-    for (int b = 0; b < D / 32; ++b)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            dvacc[b][r] = 0.f;
-            dkacc[b][r] = 0.f;
-        }
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                dvacc[kb][b][r] = 0.f;
+                dkacc[kb][b][r] = 0.f;
+            }
 
     // One query tile against this wave's keys; MASKED instances handle the
     // causal diagonal and the ragged ends, the rest carry no mask code.
@@ -219,35 +226,48 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         const float *lt = (const float *)(ot + T::TILEB);
         const float *dt = lt + T::VECB / 4;
 
-        // ---- S = Q K^T and dP = dO V^T (lane: key lr; register r: query
-        //      8*(r/4) + 4g + r%4 of the 32-query block)
-        f32x16 sacc[QB], pacc[QB];
+        // ---- S = Q K^T and dP = dO V^T (lane: key lr of block kb; register r:
+        //      query 8*(r/4) + 4g + r%4 of the 32-query block); each Q and dO
+        //      fragment read from LDS serves the KB key blocks
+        f32x16 sacc[QB][KB], pacc[QB][KB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                sacc[qb][r] = 0.f;
-                pacc[qb][r] = 0.f;
-            }
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    sacc[qb][kb][r] = 0.f;
+                    pacc[qb][kb][r] = 0.f;
+                }
 #pragma unroll
             for (int ds = 0; ds < D / 16; ++ds) {
                 const int off = qb * 32 * ROWB + roff[ds];
                 const bf16x8 aq = *(const bf16x8 *)(qt + off);
                 const bf16x8 ao = *(const bf16x8 *)(ot + off);
-                sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ds], sacc[qb], 0, 0, 0);
-                pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[ds], pacc[qb], 0, 0, 0);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kb][ds], sacc[qb][kb], 0, 0, 0);
+                    pacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[kb][ds], pacc[qb][kb], 0, 0, 0);
+                }
             }
         }
         // ---- P = exp2(S c - L2), dS = P (dP - D); masked tiles zero the pairs
         //      past Nq, past Nk, and (causal) where the key comes after the query:
-        //      query offset o in the tile is visible iff lo <= o <= hi
-        int lo = 0, hi = BR - 1;
-        if (MASKED) {
-            int64_t lo64 = CAUSAL ? mykey - qoff - q0 : 0;
-            int64_t hi64 = Nq - 1 - q0;
-            if (mykey >= Nk) hi64 = -1;
-            lo = (int)(lo64 < 0 ? 0 : (lo64 > BR ? BR : lo64));
-            hi = (int)(hi64 > BR - 1 ? BR - 1 : (hi64 < -1 ? -1 : hi64));
+        //      query offset o in the tile is visible to key block kb iff
+        //      lo[kb] <= o <= hi[kb]
+        int lo[KB], hi[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            lo[kb] = 0;
+            hi[kb] = BR - 1;
+            if (MASKED) {
+                const int64_t key = kw0 + 32 * kb + lr;
+                int64_t lo64 = CAUSAL ? key - qoff - q0 : 0;
+                int64_t hi64 = Nq - 1 - q0;
+                if (key >= Nk) hi64 = -1;
+                lo[kb] = (int)(lo64 < 0 ? 0 : (lo64 > BR ? BR : lo64));
+                hi[kb] = (int)(hi64 > BR - 1 ? BR - 1 : (hi64 < -1 ? -1 : hi64));
+            }
         }
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
@@ -257,30 +277,39 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
                 const f32x4 lv = *(const f32x4 *)(lt + qi);
                 const f32x4 dv = *(const f32x4 *)(dt + qi);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * r4 + e;
-                    float p = fast_exp2(fmaf(sacc[qb][r], c, -lv[e]));
-                    if (MASKED && (qi + e < lo || qi + e > hi)) p = 0.f;
-                    sacc[qb][r] = p;
-                    pacc[qb][r] = p * (pacc[qb][r] - dv[e]);
-                }
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * r4 + e;
+                        float p = fast_exp2(fmaf(sacc[qb][kb][r], c, -lv[e]));
+                        if (MASKED && (qi + e < lo[kb] || qi + e > hi[kb])) p = 0.f;
+                        sacc[qb][kb][r] = p;
+                        pacc[qb][kb][r] = p * (pacc[qb][kb][r] - dv[e]);
+                    }
             }
         }
         // ---- dV^T += dO^T P and dK^T += Q^T dS.  B operand (k-step kq of 16
         //      queries) = registers 8h..8h+7 of block kq/2, so k-slot (g, e) is
         //      query 8*(e/4) + 4g + e%4 of the step; the transposed A operand is
-        //      read in the same slot order.
+        //      read in the same slot order and serves the KB key blocks.
 #pragma unroll
         for (int kq = 0; kq < BR / 16; ++kq) {
-            const bf16x8 pb = pack8(sacc[kq >> 1], 8 * (kq & 1));
-            const bf16x8 sb = pack8(pacc[kq >> 1], 8 * (kq & 1));
+            bf16x8 pb[KB], sb[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                pb[kb] = pack8(sacc[kq >> 1][kb], 8 * (kq & 1));
+                sb[kb] = pack8(pacc[kq >> 1][kb], 8 * (kq & 1));
+            }
 #pragma unroll
             for (int b = 0; b < D / 32; ++b) {
                 const int off = kq * 16 * ROWB;
                 const bf16x8 ao = tr_pair<ROWB>(ot + off, toff[b]);
                 const bf16x8 aq = tr_pair<ROWB>(qt + off, toff[b]);
-                dvacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb, dvacc[b], 0, 0, 0);
-                dkacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb, dkacc[b], 0, 0, 0);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    dvacc[kb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[kb], dvacc[kb][b], 0, 0, 0);
+                    dkacc[kb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb[kb], dkacc[kb][b], 0, 0, 0);
+                }
             }
         }
     };
@@ -318,7 +347,7 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         const uint8_t *qt = smem + (idx % ST) * T::STAGEB;
         // the mask is needed on the causal diagonal and at the ragged ends only
         const bool need_mask =
-            (q0 + BR > Nq) || (kw0 + 32 > Nk) || (CAUSAL && q0 + qoff < kw0 + 31);
+            (q0 + BR > Nq) || (kw0 + KW > Nk) || (CAUSAL && q0 + qoff < kw0 + KW - 1);
         if (need_mask)
             tile(qt, q0, std::true_type{});
         else
@@ -328,24 +357,28 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
 #if FA_STATS
     if (lane == 0 && kw0 < Nk) atomicAdd(&g_bwd_stats[3], (unsigned long long)st_tiles);
 #endif
-    // ---- epilogue: dK = scale * dK_acc, dV = dV_acc (lane: key lr; register r:
-    //      column 32b + 8*(r/4) + 4g + r%4)
-    if (mykey < Nk) {
-        uint16_t *dKr = dK + (bh * Nk + mykey) * D;
-        uint16_t *dVr = dV + (bh * Nk + mykey) * D;
+    // ---- epilogue: dK = scale * dK_acc, dV = dV_acc (lane: key lr of block kb;
+    //      register r: column 32b + 8*(r/4) + 4g + r%4)
 #pragma unroll
-        for (int b = 0; b < D / 32; ++b)
+    for (int kb = 0; kb < KB; ++kb) {
+        const int64_t key = kw0 + 32 * kb + lr;
+        if (key < Nk) {
+            uint16_t *dKr = dK + (bh * Nk + key) * D;
+            uint16_t *dVr = dV + (bh * Nk + key) * D;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int col = b * 32 + 8 * t + 4 * g;
-                const u32x2 wk = {pack_bf16x2(scale * dkacc[b][4 * t], scale * dkacc[b][4 * t + 1]),
-                                  pack_bf16x2(scale * dkacc[b][4 * t + 2],
-                                              scale * dkacc[b][4 * t + 3])};
-                const u32x2 wv = {pack_bf16x2(dvacc[b][4 * t], dvacc[b][4 * t + 1]),
-                                  pack_bf16x2(dvacc[b][4 * t + 2], dvacc[b][4 * t + 3])};
-                *(u32x2 *)(dKr + col) = wk;
-                *(u32x2 *)(dVr + col) = wv;
-            }
+            for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int col = b * 32 + 8 * t + 4 * g;
+                    const f32x16 &ka = dkacc[kb][b], &va = dvacc[kb][b];
+                    const u32x2 wk = {pack_bf16x2(scale * ka[4 * t], scale * ka[4 * t + 1]),
+                                      pack_bf16x2(scale * ka[4 * t + 2], scale * ka[4 * t + 3])};
+                    const u32x2 wv = {pack_bf16x2(va[4 * t], va[4 * t + 1]),
+                                      pack_bf16x2(va[4 * t + 2], va[4 * t + 3])};
+                    *(u32x2 *)(dKr + col) = wk;
+                    *(u32x2 *)(dVr + col) = wv;
+                }
+        }
     }
 }
 
@@ -566,17 +599,31 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 #define FA_BWD_DQ_BC64 128
 #define FA_BWD_DQ_ST64 2
 #endif
+#ifndef FA_BWD_DKDV_KB64  // 32-key blocks per wave in the dK/dV pass, d = 64
+#define FA_BWD_DKDV_KB64 1
+#endif
+
+template <int D, bool CAUSAL>
+struct DkdvChoice {
+    // Two 32-key blocks per wave halve the LDS reads per product, but need more
+    // than 256 registers, so one wave per SIMD and 32-query tiles; measured
+    // 1.3x slower at 2 x 16 heads x 4096 causal (the compiler moves the score
+    // tiles between the two register files on every tile).  With one block the
+    // non-causal d = 64 instance keeps 32-query tiles: with 64 it needs more
+    // than 256 registers.
+    static constexpr int KB = D == 64 ? FA_BWD_DKDV_KB64 : 1;
+    static constexpr int BR = KB == 2 ? 32 : (D == 64 && CAUSAL ? FA_BWD_DKDV_BR64 : 32);
+    static constexpr int ST = D == 64 ? FA_BWD_DKDV_ST64 : 2;
+};
 
 template <int D, bool CAUSAL>
 hipError_t launch_main(const BwdArgs &a, float *L2, hipStream_t s) {
-    // the non-causal d = 64 instance keeps 32-query tiles: with 64 it needs more
-    // than 256 registers
-    constexpr int BR = D == 64 && CAUSAL ? FA_BWD_DKDV_BR64 : 32;
-    constexpr int ST = D == 64 ? FA_BWD_DKDV_ST64 : 2;
+    using C = DkdvChoice<D, CAUSAL>;
+    constexpr int BR = C::BR, ST = C::ST, KB = C::KB;
     constexpr int BC = D == 64 ? FA_BWD_DQ_BC64 : 32;
     constexpr int STQ = D == 64 ? FA_BWD_DQ_ST64 : 2;
-    const int nkt = (int)((a.Nk + DkdvCfg<D, BR, ST>::KEYS - 1) / DkdvCfg<D, BR, ST>::KEYS);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BR, ST, CAUSAL>), dim3((unsigned)(a.B * a.H * nkt)),
+    const int nkt = (int)((a.Nk + DkdvCfg<D, BR, ST, KB>::KEYS - 1) / DkdvCfg<D, BR, ST, KB>::KEYS);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BR, ST, KB, CAUSAL>), dim3((unsigned)(a.B * a.H * nkt)),
                        dim3(kThreads), 0, s, (const uint16_t *)a.Q, (const uint16_t *)a.K,
                        (const uint16_t *)a.V, (const uint16_t *)a.dO, L2, a.D, (uint16_t *)a.dK,
                        (uint16_t *)a.dV, a.Nq, a.Nk, a.q_start, nkt, a.scale, a.scale * kLog2e);
@@ -603,8 +650,8 @@ hipError_t stats_bwd(unsigned long long *host, bool reset) {
 
 void bwd_bf16_tiles(int64_t d, int causal, int64_t *kv_rows, int64_t *kv_cols, int64_t *q_rows,
                     int64_t *q_cols) {
-    *kv_rows = 32;
-    *kv_cols = d == 64 && causal ? FA_BWD_DKDV_BR64 : 32;
+    *kv_rows = d == 64 ? (causal ? 32 * DkdvChoice<64, true>::KB : 32 * DkdvChoice<64, false>::KB) : 32;
+    *kv_cols = d == 64 ? (causal ? DkdvChoice<64, true>::BR : DkdvChoice<64, false>::BR) : 32;
     *q_rows = 32;
     *q_cols = d == 64 ? FA_BWD_DQ_BC64 : 32;
 }

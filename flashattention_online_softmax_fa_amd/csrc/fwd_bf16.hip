@@ -7,7 +7,7 @@
 // after its last query under the causal mask, divides once at the end and
 // writes L = m + log l.
 //
-// Work split.  One workgroup (4 waves) per (batch*head, query tile); each
+// Work split.  One workgroup (W waves) per (batch*head, query tile); each
 // wave owns 32*QB queries, whose Q rows stay in registers.  Key/value tiles of
 // BC keys stream from HBM straight into an LDS ring of STAGES slots with
 // global_load_lds_dwordx4 (no register staging); each wave issues its share of
@@ -53,12 +53,16 @@
 #define FA_FWD_BC128 32
 #define FA_FWD_ST128 4
 #endif
+#ifndef FA_FWD_WG64  // waves per workgroup
+#define FA_FWD_WG64 4
+#endif
+#ifndef FA_FWD_WG128
+#define FA_FWD_WG128 4
+#endif
 
 namespace fa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr float kMargin = 8.f;
 
 #if FA_STATS
@@ -66,31 +70,39 @@ __device__ unsigned long long g_fwd_stats[kStatCount];
 #endif         // base-2 headroom before the reference max is raised
 
 // D: head dimension; QB: 32-query blocks per wave (each K / V^T fragment read
-// from LDS feeds QB matrix-core products); BC: keys per tile.
-template <int D, int QB, int BC_, int STAGES_>
+// from LDS feeds QB matrix-core products); BC: keys per tile; W: waves per
+// workgroup.  With W = 8 the two waves that share a SIMD belong to the same
+// workgroup and keep pace through its barriers; with W = 4 two workgroups
+// share each CU and the older one is issued first, so the younger one ends a
+// single-round launch alone.  Measured, the two end up within 2 % of each
+// other (the lockstep costs about what the lone tail does); W = 4 is kept.
+template <int D, int QB, int BC_, int STAGES_, int W_>
 struct Tile {
+    static constexpr int W = W_;
     static constexpr int BC = BC_;
     static constexpr int QW = 32 * QB;               // queries per wave
-    static constexpr int BR = kWaves * QW;           // queries per workgroup
+    static constexpr int BR = W * QW;                // queries per workgroup
     static constexpr int CH = D / 8;                 // 16-byte chunks per row
     static constexpr int ROWB = D * 2;               // bytes per row
     static constexpr int TILEB = BC * ROWB;          // bytes of one K or V tile
+    static constexpr int NB = TILEB / 1024;          // 1 KiB blocks per K or V tile
     static constexpr int STAGES = STAGES_;           // LDS ring depth
-    static constexpr int IPW = TILEB / 1024 / kWaves;  // 1 KiB loads per wave per tensor
+    static constexpr int LPW = 2 * NB / W;           // 1 KiB loads per wave per tile (K and V)
     static constexpr int RPI = 1024 / ROWB;          // rows per 1 KiB load
-    static_assert(IPW >= 1, "tile too small for one load per wave");
+    static_assert(LPW >= 1 && LPW * W == 2 * NB, "K and V tiles split evenly over the waves");
     static_assert(STAGES >= 3 && STAGES <= 8, "ring depth");
     static_assert(BC % 32 == 0, "32-key blocks");
+    static_assert(W == 4 || W == 8, "4 or 8 waves");
 };
 
-template <int D, int QB, int BC, int ST, bool CAUSAL, bool POS_SCALE>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(D * QB >= 256 ? 1 : (D == 64 ? FA_FWD_W64 : FA_FWD_W128), 4)))
+template <int D, int QB, int BC, int ST, int W, bool CAUSAL, bool POS_SCALE>
+__global__ __launch_bounds__(W * 64)
+__attribute__((amdgpu_waves_per_eu(D * QB >= 256 ? 1 : (W == 8 ? 2 : (D == 64 ? FA_FWD_W64 : FA_FWD_W128)), 4)))
 void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                      const uint16_t *__restrict__ V, uint16_t *__restrict__ O,
                      float *__restrict__ L, int64_t Nq, int64_t Nk, int64_t qoff, int nqt,
                      float c) {
-    using T = Tile<D, QB, BC, ST>;
+    using T = Tile<D, QB, BC, ST, W>;
     constexpr int S = T::STAGES;
     constexpr int KB = BC / 32;  // 32-key blocks per tile
     __shared__ __attribute__((aligned(1024))) uint8_t smem[S * 2 * T::TILEB];
@@ -127,39 +139,38 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         nfull = (int)(f < nkt_w ? f : nkt_w);
     }
 
-    // ---- ring loads: this lane fills LDS chunk `lane` of each of its IPW 1 KiB
-    //      blocks with logical chunk (lane % CH) ^ f(row) of that row
-    int ld_row[T::IPW], ld_off[T::IPW];
+    // ---- ring loads: load j = wave * LPW + u of a step fills 1 KiB block j % NB
+    //      of the K (j < NB) or V tile; this lane writes LDS chunk `lane` of the
+    //      block with logical chunk (lane % CH) ^ f(row) of that row
+    int ld_row[T::LPW], ld_off[T::LPW];
 #pragma unroll
-    for (int u = 0; u < T::IPW; ++u) {
-        const int row = (wave * T::IPW + u) * T::RPI + lane / T::CH;
+    for (int u = 0; u < T::LPW; ++u) {
+        const int row = ((wave * T::LPW + u) % T::NB) * T::RPI + lane / T::CH;
         ld_row[u] = row;
         ld_off[u] = chunk_off<T::ROWB>(row, lane % T::CH);
     }
     auto issue = [&](int t, int st) {
         const int64_t kv0 = (int64_t)t * BC;
-        uint8_t *kb = smem + st * 2 * T::TILEB + wave * T::IPW * 1024;
-        uint8_t *vb = kb + T::TILEB;
         const uint8_t *kt = (const uint8_t *)(Kh + kv0 * D);
         const uint8_t *vt = (const uint8_t *)(Vh + kv0 * D);
-        if (kv0 + BC <= Nk) {
+        const bool full = kv0 + BC <= Nk;
 #pragma unroll
-            for (int u = 0; u < T::IPW; ++u) {
-                dma16_s(kt, (uint32_t)ld_off[u], kb + u * 1024);
-                dma16_s(vt, (uint32_t)ld_off[u], vb + u * 1024);
-            }
-        } else {  // rows past Nk re-read the last key; they are masked
-#pragma unroll
-            for (int u = 0; u < T::IPW; ++u) {
+        for (int u = 0; u < T::LPW; ++u) {
+            const int j = wave * T::LPW + u;  // wave-uniform
+            const bool is_v = j >= T::NB;
+            const uint8_t *src = is_v ? vt : kt;
+            uint8_t *dst = smem + st * 2 * T::TILEB + j * 1024;  // V follows K in the slot
+            if (full) {
+                dma16_s(src, (uint32_t)ld_off[u], dst);
+            } else {  // rows past Nk re-read the last key; they are masked
                 const int64_t key = kv0 + ld_row[u];
                 const int64_t back = key < Nk ? 0 : (key - (Nk - 1)) * T::ROWB;
-                dma16(kt + ld_off[u] - back, kb + u * 1024);
-                dma16(vt + ld_off[u] - back, vb + u * 1024);
+                dma16(src + ld_off[u] - back, dst);
             }
         }
     };
     // wait until at most n ring steps of this wave's loads are still in flight
-    auto wait_pending = [&](int n) { wait_steps<2 * T::IPW, S - 2>(n); };
+    auto wait_pending = [&](int n) { wait_steps<T::LPW, S - 2>(n); };
 
     // ---- per-lane constants of the LDS reads
     // K (A operand of S^T): row kb*32 + lr, logical chunk 2*ds + g
@@ -440,26 +451,27 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
 #endif
 }
 
-template <int D, int QB, int BC, int ST, bool CAUSAL>
+template <int D, int QB, int BC, int ST, int W, bool CAUSAL>
 hipError_t launch_d(const FwdArgs &a, hipStream_t s) {
-    using T = Tile<D, QB, BC, ST>;
+    using T = Tile<D, QB, BC, ST, W>;
     const int nqt = (int)((a.Nq + T::BR - 1) / T::BR);
     const dim3 grid((unsigned)(a.B * a.H * nqt));
     const float c = a.scale * kLog2e;
     if (a.scale > 0.f)
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BC, ST, CAUSAL, true>), grid, dim3(kThreads), 0, s,
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BC, ST, W, CAUSAL, true>), grid, dim3(W * 64), 0, s,
                            (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
                            (uint16_t *)a.O, a.L, a.Nq, a.Nk, a.q_start, nqt, c);
     else
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BC, ST, CAUSAL, false>), grid, dim3(kThreads), 0,
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BC, ST, W, CAUSAL, false>), grid, dim3(W * 64), 0,
                            s, (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
                            (uint16_t *)a.O, a.L, a.Nq, a.Nk, a.q_start, nqt, c);
     return hipGetLastError();
 }
 
 // Tile configurations (chosen by measurement on MI355X).
-constexpr int kQB64 = FA_FWD_QB64, kBC64 = FA_FWD_BC64, kST64 = FA_FWD_ST64;
-constexpr int kQB128 = FA_FWD_QB128, kBC128 = FA_FWD_BC128, kST128 = FA_FWD_ST128;
+constexpr int kQB64 = FA_FWD_QB64, kBC64 = FA_FWD_BC64, kST64 = FA_FWD_ST64, kWG64 = FA_FWD_WG64;
+constexpr int kQB128 = FA_FWD_QB128, kBC128 = FA_FWD_BC128, kST128 = FA_FWD_ST128,
+              kWG128 = FA_FWD_WG128;
 
 }  // namespace
 
@@ -473,17 +485,17 @@ hipError_t stats_fwd(unsigned long long *host, bool reset) {
 }
 
 void fwd_bf16_tile(int64_t d, int64_t *rows, int64_t *cols) {
-    *rows = d == 128 ? Tile<128, kQB128, kBC128, kST128>::QW : Tile<64, kQB64, kBC64, kST64>::QW;
+    *rows = d == 128 ? Tile<128, kQB128, kBC128, kST128, kWG128>::QW : Tile<64, kQB64, kBC64, kST64, kWG64>::QW;
     *cols = d == 128 ? kBC128 : kBC64;
 }
 #endif
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s) {
     if (a.d == 128)
-        return a.causal ? launch_d<128, kQB128, kBC128, kST128, true>(a, s)
-                        : launch_d<128, kQB128, kBC128, kST128, false>(a, s);
-    return a.causal ? launch_d<64, kQB64, kBC64, kST64, true>(a, s)
-                    : launch_d<64, kQB64, kBC64, kST64, false>(a, s);
+        return a.causal ? launch_d<128, kQB128, kBC128, kST128, kWG128, true>(a, s)
+                        : launch_d<128, kQB128, kBC128, kST128, kWG128, false>(a, s);
+    return a.causal ? launch_d<64, kQB64, kBC64, kST64, kWG64, true>(a, s)
+                    : launch_d<64, kQB64, kBC64, kST64, kWG64, false>(a, s);
 }
 
 }  // namespace fa
