@@ -128,7 +128,7 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
                      const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
                      const float *__restrict__ L2, const float *__restrict__ Dv,
                      uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int64_t Nq, int64_t Nk,
-                     int64_t qoff, int nkt, float scale, float c) {
+                     int64_t qoff, int nkt, uint32_t group, float scale, float c) {
     using T = DkdvCfg<D, BR, ST, KB>;
     constexpr int QB = T::QB, ROWB = T::ROWB;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * T::STAGEB];
@@ -136,7 +136,7 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = tid >> 6;
     const int g = lane >> 5, lr = lane & 31;
-    const TileId tid_ = tile_order(blockIdx.x, gridDim.x / (uint32_t)nkt, (uint32_t)nkt);
+    const TileId tid_ = tile_order(blockIdx.x, gridDim.x / (uint32_t)nkt, (uint32_t)nkt, group);
     const int64_t bh = tid_.head;
     const int kt = (int)tid_.rank;  // causal: early keys are seen by the most queries
     const int64_t k0 = (int64_t)kt * T::KEYS;
@@ -403,7 +403,7 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
                    const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
                    const float *__restrict__ L2, const float *__restrict__ Dv,
                    uint16_t *__restrict__ dQ, int64_t Nq, int64_t Nk, int64_t qoff, int nqt,
-                   float scale, float c) {
+                   uint32_t group, float scale, float c) {
     using T = DqCfg<D, BC, ST>;
     constexpr int ROWB = T::ROWB;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * 2 * T::TILEB];
@@ -411,7 +411,7 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, lr = lane & 31;
-    const TileId tid_ = tile_order(blockIdx.x, gridDim.x / (uint32_t)nqt, (uint32_t)nqt);
+    const TileId tid_ = tile_order(blockIdx.x, gridDim.x / (uint32_t)nqt, (uint32_t)nqt, group);
     const int64_t bh = tid_.head;
     const int qt = CAUSAL ? nqt - 1 - (int)tid_.rank : (int)tid_.rank;  // causal: late queries see the most keys
     const int64_t q0 = (int64_t)qt * T::BR;
@@ -626,14 +626,16 @@ hipError_t launch_main(const BwdArgs &a, float *L2, hipStream_t s) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, BR, ST, KB, CAUSAL>), dim3((unsigned)(a.B * a.H * nkt)),
                        dim3(kThreads), 0, s, (const uint16_t *)a.Q, (const uint16_t *)a.K,
                        (const uint16_t *)a.V, (const uint16_t *)a.dO, L2, a.D, (uint16_t *)a.dK,
-                       (uint16_t *)a.dV, a.Nq, a.Nk, a.q_start, nkt, a.scale, a.scale * kLog2e);
+                       (uint16_t *)a.dV, a.Nq, a.Nk, a.q_start, nkt,
+                       tile_group(a.B * a.H), a.scale, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nqt = (int)((a.Nq + DqCfg<D, BC, STQ>::BR - 1) / DqCfg<D, BC, STQ>::BR);
     hipLaunchKernelGGL((bwd_dq_kernel<D, BC, STQ, CAUSAL>), dim3((unsigned)(a.B * a.H * nqt)),
                        dim3(kThreads), 0, s, (const uint16_t *)a.Q, (const uint16_t *)a.K,
                        (const uint16_t *)a.V, (const uint16_t *)a.dO, L2, a.D, (uint16_t *)a.dQ,
-                       a.Nq, a.Nk, a.q_start, nqt, a.scale, a.scale * kLog2e);
+                       a.Nq, a.Nk, a.q_start, nqt, tile_group(a.B * a.H), a.scale,
+                       a.scale * kLog2e);
     return hipGetLastError();
 }
 

@@ -178,31 +178,37 @@ __device__ __forceinline__ void dma4(const void *src, uint8_t *dst) { dma4(src, 
 
 // Workgroups are dealt round-robin over the 8 XCDs (bid % 8).  Workgroup
 // `bid` of a grid of heads * tiles -> (head, tile rank), rank 0 = the tile
-// with the most work.  When the heads split evenly over the XCDs, each XCD
-// takes a contiguous group of heads, so that the tiles sharing a head's
-// operands share that XCD's L2; inside the group (or over all heads when they
-// do not split evenly) the order is rank-major, so the heaviest tiles of every
-// head start first and the light ones fill the end of the launch.  (Head-major
-// order would leave one slot per CU running a head's heavy tiles while the
-// other has finished: about a third of a causal launch idle at the end.)
-#ifndef FA_TILE_MAJOR
-#define FA_TILE_MAJOR 1
-#endif
+// with the most work.  When the heads split evenly over the XCDs each XCD
+// takes a contiguous range of heads, so that the tiles sharing a head's
+// streamed operands share that XCD's L2.  The range is walked in groups of
+// `group` heads (tile_group), rank-major inside a group: the heaviest tiles
+// of the group's heads start first and the light ones fill the end, while the
+// operands of only `group` heads are live in the L2 at a time.  (Head-major
+// order, group = 1, leaves one slot of a CU running a head's heavy tiles while
+// the other has finished: about a third of a causal dK/dV or dQ launch idled.)
 struct TileId {
     uint32_t head, rank;
 };
-__device__ __forceinline__ TileId tile_order(uint32_t bid, uint32_t heads, uint32_t tiles) {
-#if FA_TILE_MAJOR
+__device__ __forceinline__ TileId tile_order(uint32_t bid, uint32_t heads, uint32_t tiles,
+                                             uint32_t group) {
+    uint32_t x = 0, r = bid, hx = heads;
     if (heads % 8u == 0) {
-        const uint32_t G = heads / 8u, r = bid / 8u;
-        return {(bid % 8u) * G + r % G, r / G};
+        x = bid % 8u;
+        r = bid / 8u;
+        hx = heads / 8u;
     }
-    return {bid % heads, bid / heads};
-#else
-    const uint32_t nblocks = heads * tiles;
-    const uint32_t lid = nblocks % 8u ? bid : (bid % 8u) * (nblocks / 8u) + bid / 8u;
-    return {lid / tiles, lid % tiles};
-#endif
+    const uint32_t per = group * tiles;
+    const uint32_t gi = r / per, w = r % per;
+    return {x * hx + gi * group + w % group, w / group};
 }
+
+// Heads per group for tile_order: every head an XCD takes (all heads when
+// they do not split over the XCDs).  Smaller groups, sized so that a group's
+// K and V (or Q and dO) fit in half of an XCD's L2, cut the HBM re-reads of
+// the causal d = 128 forward from 3.7x to about 1x the algorithmic bytes but
+// measured slower in every pass (forward 562 vs 545 us, backward 297 vs
+// 274 us): the balance of the launch matters more than the re-reads, which
+// use HBM bandwidth the matrix-core-bound kernels leave idle.
+inline uint32_t tile_group(int64_t heads) { return (uint32_t)(heads % 8 == 0 ? heads / 8 : heads); }
 
 }  // namespace fa

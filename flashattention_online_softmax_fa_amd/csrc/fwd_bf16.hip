@@ -101,7 +101,7 @@ __attribute__((amdgpu_waves_per_eu(D * QB >= 256 ? 1 : (W == 8 ? 2 : (D == 64 ? 
 void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                      const uint16_t *__restrict__ V, uint16_t *__restrict__ O,
                      float *__restrict__ L, int64_t Nq, int64_t Nk, int64_t qoff, int nqt,
-                     float c) {
+                     uint32_t group, float c) {
     using T = Tile<D, QB, BC, ST, W>;
     constexpr int S = T::STAGES;
     constexpr int KB = BC / 32;  // 32-key blocks per tile
@@ -111,7 +111,7 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, lr = lane & 31, s16 = lane & 15, G = lane >> 4;
     const int xaddr = (lane ^ 32) << 2;  // ds_bpermute address of the other half of the row
-    const TileId tid_ = tile_order(blockIdx.x, gridDim.x / (uint32_t)nqt, (uint32_t)nqt);
+    const TileId tid_ = tile_order(blockIdx.x, gridDim.x / (uint32_t)nqt, (uint32_t)nqt, group);
     const int64_t bh = tid_.head;
     const int qt = CAUSAL ? nqt - 1 - (int)tid_.rank : (int)tid_.rank;  // causal: late queries see the most keys
     const int64_t q0 = (int64_t)qt * T::BR;
@@ -457,14 +457,15 @@ hipError_t launch_d(const FwdArgs &a, hipStream_t s) {
     const int nqt = (int)((a.Nq + T::BR - 1) / T::BR);
     const dim3 grid((unsigned)(a.B * a.H * nqt));
     const float c = a.scale * kLog2e;
+    const uint32_t group = tile_group(a.B * a.H);
     if (a.scale > 0.f)
         hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BC, ST, W, CAUSAL, true>), grid, dim3(W * 64), 0, s,
                            (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
-                           (uint16_t *)a.O, a.L, a.Nq, a.Nk, a.q_start, nqt, c);
+                           (uint16_t *)a.O, a.L, a.Nq, a.Nk, a.q_start, nqt, group, c);
     else
         hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BC, ST, W, CAUSAL, false>), grid, dim3(W * 64), 0,
                            s, (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
-                           (uint16_t *)a.O, a.L, a.Nq, a.Nk, a.q_start, nqt, c);
+                           (uint16_t *)a.O, a.L, a.Nq, a.Nk, a.q_start, nqt, group, c);
     return hipGetLastError();
 }
 
