@@ -11,14 +11,15 @@
 // traffic per call at 2 x 16 heads x 4096 tokens), which costs more than
 // recomputing two of the five products.  The result is also deterministic.
 //
-// Three launches on the caller's stream:
-//   bwd_pre_kernel   D = rowsum(dO * O) and L2 = L * log2(e), fp32;
-//   bwd_dkdv_kernel  one workgroup per (batch*head, 128-key tile), 4 waves of 32
-//                    keys, K and V in registers; Q, dO, L2 and D tiles of the
-//                    query tiles that can see its keys stream through an LDS ring;
+// Two launches on the caller's stream:
 //   bwd_dq_kernel    one workgroup per (batch*head, 128-query tile), 4 waves of
 //                    32 queries, Q and dO in registers; K and V tiles of the key
-//                    tiles its queries can see stream through an LDS ring.
+//                    tiles its queries can see stream through an LDS ring.  It
+//                    also forms D = rowsum(dO * O) and L2 = L * log2(e) of its
+//                    queries and writes them to the workspace;
+//   bwd_dkdv_kernel  one workgroup per (batch*head, key tile), 4 waves of 32
+//                    keys, K and V in registers; Q, dO, L2 and D tiles of the
+//                    query tiles that can see its keys stream through an LDS ring.
 // Both rings are filled with global_load_lds_dwordx4 into row-major,
 // chunk-swizzled tiles (see fa_device.h), one barrier per tile.
 //
@@ -68,38 +69,6 @@ __device__ __forceinline__ u32x4 load_row16(const uint16_t *base, int64_t row, i
     const int64_t r = row < rows ? row : rows - 1;
     const u32x4 w = *(const u32x4 *)(base + r * D + col8 * 8);
     return row < rows ? w : u32x4{0u, 0u, 0u, 0u};
-}
-
-// ---------------------------------------------------------------------------
-// D = rowsum(dO * O) and L2 = L * log2(e) (fp32).
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict__ O,
-                                                      const uint16_t *__restrict__ dO,
-                                                      const float *__restrict__ L,
-                                                      float *__restrict__ Dv,
-                                                      float *__restrict__ L2, int64_t rows) {
-    constexpr int LPR = D / 8;  // lanes per row (16-byte chunks)
-    const int64_t chunk = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t row = chunk / LPR;
-    const int sub = (int)(chunk % LPR);
-    float s = 0.f;
-    if (row < rows) {
-        const u32x4 o = *(const u32x4 *)(O + row * D + sub * 8);
-        const u32x4 g = *(const u32x4 *)(dO + row * D + sub * 8);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            s = fmaf(bf16_lo(o[w]), bf16_lo(g[w]), s);
-            s = fmaf(bf16_hi(o[w]), bf16_hi(g[w]), s);
-        }
-    }
-    // sum over the LPR lanes of the row (aligned groups of 8 or 16 lanes)
-#pragma unroll
-    for (int o = 1; o < LPR; o <<= 1) s += __shfl_xor(s, o);
-    if (row < rows && sub == 0) {
-        Dv[row] = s;
-        L2[row] = L[row] * kLog2e;
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -400,8 +369,9 @@ struct DqCfg {
 template <int D, int BC, int ST, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-                   const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
-                   const float *__restrict__ L2, const float *__restrict__ Dv,
+                   const uint16_t *__restrict__ V, const uint16_t *__restrict__ O,
+                   const uint16_t *__restrict__ dO, const float *__restrict__ L,
+                   float *__restrict__ L2, float *__restrict__ Dv,
                    uint16_t *__restrict__ dQ, int64_t Nq, int64_t Nk, int64_t qoff, int nqt,
                    uint32_t group, float scale, float c) {
     using T = DqCfg<D, BC, ST>;
@@ -435,9 +405,29 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
         qf[ds] = __builtin_bit_cast(bf16x8, load_row16(Q + bh * Nq * D, qrow, Nq, D, ds * 2 + g));
         of[ds] = __builtin_bit_cast(bf16x8, load_row16(dO + bh * Nq * D, qrow, Nq, D, ds * 2 + g));
     }
+    // D = rowsum(dO * O) and L2 = L * log2(e) of this lane's query: the lane
+    // holds half of the row (chunks 2ds + g), lane ^ 32 the other half.  The
+    // dK/dV pass, launched after this one, reads both from the workspace.
     const int64_t qc = qrow < Nq ? qrow : Nq - 1;
-    const float l2 = qrow < Nq ? L2[bh * Nq + qc] : INFINITY;  // padded row: P = 0
-    const float dq = qrow < Nq ? Dv[bh * Nq + qc] : 0.f;
+    float dsum = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+        const u32x4 o = load_row16(O + bh * Nq * D, qrow, Nq, D, ds * 2 + g);
+        const u32x4 w = __builtin_bit_cast(u32x4, of[ds]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            dsum = fmaf(bf16_lo(o[e]), bf16_lo(w[e]), dsum);
+            dsum = fmaf(bf16_hi(o[e]), bf16_hi(w[e]), dsum);
+        }
+    }
+    dsum += __shfl_xor(dsum, 32);
+    const float lrow = L[bh * Nq + qc];
+    if (g == 0 && qrow < Nq) {
+        L2[bh * Nq + qc] = lrow * kLog2e;
+        Dv[bh * Nq + qc] = dsum;
+    }
+    const float l2 = qrow < Nq ? lrow * kLog2e : INFINITY;  // padded row: P = 0
+    const float dq = qrow < Nq ? dsum : 0.f;
 
     auto ld_row = [&](int u) { return (wave * T::IPW + u) * T::RPI + lane / T::CH; };
     uint32_t ld_off[T::IPW];  // byte offset of this lane's load within a tile
@@ -617,24 +607,25 @@ struct DkdvChoice {
 };
 
 template <int D, bool CAUSAL>
-hipError_t launch_main(const BwdArgs &a, float *L2, hipStream_t s) {
+hipError_t launch_main(const BwdArgs &a, hipStream_t s) {
     using C = DkdvChoice<D, CAUSAL>;
     constexpr int BR = C::BR, ST = C::ST, KB = C::KB;
     constexpr int BC = D == 64 ? FA_BWD_DQ_BC64 : 32;
     constexpr int STQ = D == 64 ? FA_BWD_DQ_ST64 : 2;
-    const int nkt = (int)((a.Nk + DkdvCfg<D, BR, ST, KB>::KEYS - 1) / DkdvCfg<D, BR, ST, KB>::KEYS);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BR, ST, KB, CAUSAL>), dim3((unsigned)(a.B * a.H * nkt)),
-                       dim3(kThreads), 0, s, (const uint16_t *)a.Q, (const uint16_t *)a.K,
-                       (const uint16_t *)a.V, (const uint16_t *)a.dO, L2, a.D, (uint16_t *)a.dK,
-                       (uint16_t *)a.dV, a.Nq, a.Nk, a.q_start, nkt,
-                       tile_group(a.B * a.H), a.scale, a.scale * kLog2e);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // the dQ pass first: it also writes D and L2, which the dK/dV pass reads
     const int nqt = (int)((a.Nq + DqCfg<D, BC, STQ>::BR - 1) / DqCfg<D, BC, STQ>::BR);
     hipLaunchKernelGGL((bwd_dq_kernel<D, BC, STQ, CAUSAL>), dim3((unsigned)(a.B * a.H * nqt)),
                        dim3(kThreads), 0, s, (const uint16_t *)a.Q, (const uint16_t *)a.K,
-                       (const uint16_t *)a.V, (const uint16_t *)a.dO, L2, a.D, (uint16_t *)a.dQ,
-                       a.Nq, a.Nk, a.q_start, nqt, tile_group(a.B * a.H), a.scale,
+                       (const uint16_t *)a.V, (const uint16_t *)a.O, (const uint16_t *)a.dO, a.L,
+                       a.L2, a.D, (uint16_t *)a.dQ, a.Nq, a.Nk, a.q_start, nqt,
+                       tile_group(a.B * a.H), a.scale, a.scale * kLog2e);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nkt = (int)((a.Nk + DkdvCfg<D, BR, ST, KB>::KEYS - 1) / DkdvCfg<D, BR, ST, KB>::KEYS);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BR, ST, KB, CAUSAL>), dim3((unsigned)(a.B * a.H * nkt)),
+                       dim3(kThreads), 0, s, (const uint16_t *)a.Q, (const uint16_t *)a.K,
+                       (const uint16_t *)a.V, (const uint16_t *)a.dO, a.L2, a.D, (uint16_t *)a.dK,
+                       (uint16_t *)a.dV, a.Nq, a.Nk, a.q_start, nkt, tile_group(a.B * a.H), a.scale,
                        a.scale * kLog2e);
     return hipGetLastError();
 }
@@ -660,21 +651,9 @@ void bwd_bf16_tiles(int64_t d, int causal, int64_t *kv_rows, int64_t *kv_cols, i
 #endif
 
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s) {
-    const int64_t rows = a.B * a.H * a.Nq;
-    const int64_t chunks = rows * (a.d / 8);
-    const dim3 pre_grid((unsigned)((chunks + 255) / 256));
-    float *L2 = a.L2;
     if (a.d == 128)
-        hipLaunchKernelGGL(bwd_pre_kernel<128>, pre_grid, dim3(256), 0, s, (const uint16_t *)a.O,
-                           (const uint16_t *)a.dO, a.L, a.D, L2, rows);
-    else
-        hipLaunchKernelGGL(bwd_pre_kernel<64>, pre_grid, dim3(256), 0, s, (const uint16_t *)a.O,
-                           (const uint16_t *)a.dO, a.L, a.D, L2, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (a.d == 128)
-        return a.causal ? launch_main<128, true>(a, L2, s) : launch_main<128, false>(a, L2, s);
-    return a.causal ? launch_main<64, true>(a, L2, s) : launch_main<64, false>(a, L2, s);
+        return a.causal ? launch_main<128, true>(a, s) : launch_main<128, false>(a, s);
+    return a.causal ? launch_main<64, true>(a, s) : launch_main<64, false>(a, s);
 }
 
 }  // namespace fa
