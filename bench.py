@@ -179,13 +179,13 @@ def io_model(run, fa_mod):
     (flash_forward's IO count in attention_kernels.py: Q read once, O and L
     written once, K and V read once per query tile, or once in total when they
     stay in cache), in bytes for bf16 tensors and an fp32 L, next to the
-    measured traffic.  The query tile is the workgroup's rows (4 wavefronts)."""
+    measured traffic.  The query tile is the workgroup's rows."""
     cfg = run["cfg"]
     B, H, Nq, Nk, d = cfg["B"], cfg["H"], cfg["Nq"], cfg["Nk"], cfg["d"]
     rows = None
     try:
         from flashattention_online_softmax_fa_amd import stats
-        rows = 4 * stats.load().tile(0, d, cfg["causal"])[0]
+        rows = stats.load().tile(3, d, cfg["causal"])[0]
     except (ImportError, OSError):
         pass
     once = B * H * (2 * Nq * d * 2 + Nq * 4)         # Q read, O written, L written

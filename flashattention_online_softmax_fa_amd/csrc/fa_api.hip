@@ -226,11 +226,11 @@ fa_status fa_stats_read(uint64_t *out) {
 
 fa_status fa_stats_tile(int kind, fa_dtype dt, int64_t d, int causal, int64_t *rows,
                         int64_t *cols) {
-    if (rows == nullptr || cols == nullptr || kind < 0 || kind > 2) return FA_ERR_INVALID_ARG;
+    if (rows == nullptr || cols == nullptr || kind < 0 || kind > 3) return FA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
     if (dt != FA_BF16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
-    if (kind == 0) {
-        fa::fwd_bf16_tile(d, rows, cols);
+    if (kind == 0 || kind == 3) {
+        fa::fwd_bf16_tile(d, kind == 3, rows, cols);
     } else {
         int64_t kr, kc, qr, qc;
         fa::bwd_bf16_tiles(d, causal, &kr, &kc, &qr, &qc);

@@ -57,7 +57,7 @@ constexpr int kStatCount = 8;
 #if FA_STATS
 hipError_t stats_fwd(unsigned long long *host, bool reset);  // copy out, or zero
 hipError_t stats_bwd(unsigned long long *host, bool reset);
-void fwd_bf16_tile(int64_t d, int64_t *rows, int64_t *cols);
+void fwd_bf16_tile(int64_t d, bool workgroup, int64_t *rows, int64_t *cols);
 void bwd_bf16_tiles(int64_t d, int causal, int64_t *kv_rows, int64_t *kv_cols, int64_t *q_rows,
                     int64_t *q_cols);
 #endif

@@ -57,8 +57,11 @@ fa_status fa_stats_read(uint64_t *out);
 /* Block shapes of the counted kernels for (dt, d, causal):
  *   kind 0: forward       -> *rows = query rows per block, *cols = keys per tile;
  *   kind 1: dK/dV pass    -> *rows = keys per block, *cols = queries per tile;
- *   kind 2: dQ pass       -> *rows = query rows per block, *cols = keys per tile.
- * FA_ERR_UNSUPPORTED unless dt = FA_BF16 and d in {64, 128}. */
+ *   kind 2: dQ pass       -> *rows = query rows per block, *cols = keys per tile;
+ *   kind 3: forward       -> *rows = query rows per workgroup (the query tile
+ *                            that streams K and V once), *cols = keys per tile.
+ * FA_ERR_INVALID_ARG for another kind; FA_ERR_UNSUPPORTED unless dt = FA_BF16
+ * and d in {64, 128}. */
 fa_status fa_stats_tile(int kind, fa_dtype dt, int64_t d, int causal, int64_t *rows,
                         int64_t *cols);
 

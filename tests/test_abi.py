@@ -206,14 +206,20 @@ def test_stats_tile_shapes():
     dbg.fa_stats_tile.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int, i64p,
                                   i64p]
     r, c = ctypes.c_int64(), ctypes.c_int64()
-    for kind in (0, 1, 2):
+    for kind in (0, 1, 2, 3):
         for d in (64, 128):
             for causal in (0, 1):
                 assert dbg.fa_stats_tile(kind, FA_BF16, d, causal, ctypes.byref(r),
                                          ctypes.byref(c)) == FA_OK
                 assert r.value >= 32 and r.value % 32 == 0 and c.value % 32 == 0
+    # a forward workgroup holds whole wavefront blocks with the same key tile
+    for d in (64, 128):
+        wr, wc = ctypes.c_int64(), ctypes.c_int64()
+        assert dbg.fa_stats_tile(0, FA_BF16, d, 0, ctypes.byref(r), ctypes.byref(c)) == FA_OK
+        assert dbg.fa_stats_tile(3, FA_BF16, d, 0, ctypes.byref(wr), ctypes.byref(wc)) == FA_OK
+        assert wr.value % r.value == 0 and wr.value >= 4 * r.value and wc.value == c.value
     assert dbg.fa_stats_tile(0, FA_F32, 64, 0, ctypes.byref(r), ctypes.byref(c)) == \
         FA_ERR_UNSUPPORTED
-    assert dbg.fa_stats_tile(3, FA_BF16, 64, 0, ctypes.byref(r), ctypes.byref(c)) == \
+    assert dbg.fa_stats_tile(4, FA_BF16, 64, 0, ctypes.byref(r), ctypes.byref(c)) == \
         FA_ERR_INVALID_ARG
     assert dbg.fa_stats_tile(0, FA_BF16, 64, 0, None, ctypes.byref(c)) == FA_ERR_INVALID_ARG
