@@ -12,16 +12,17 @@
 // recomputing two of the five products.  The result is also deterministic.
 //
 // Two launches on the caller's stream:
-//   bwd_dq_kernel    one workgroup per (batch*head, 128-query tile), 4 waves of
-//                    32 queries, Q and dO in registers; K and V tiles of the key
+//   bwd_dq_kernel    one workgroup per (batch*head, 32*W-query tile), W waves
+//                    of 32 queries, Q and dO in registers; K and V tiles of the key
 //                    tiles its queries can see stream through an LDS ring.  It
 //                    also forms D = rowsum(dO * O) and L2 = L * log2(e) of its
 //                    queries and writes them to the workspace;
-//   bwd_dkdv_kernel  one workgroup per (batch*head, key tile), 4 waves of 32
+//   bwd_dkdv_kernel  one workgroup per (batch*head, key tile), W waves of 32
 //                    keys, K and V in registers; Q, dO, L2 and D tiles of the
 //                    query tiles that can see its keys stream through an LDS ring.
 // Both rings are filled with global_load_lds_dwordx4 into row-major,
-// chunk-swizzled tiles (see fa_device.h), one barrier per tile.
+// chunk-swizzled tiles (see fa_device.h); a ring of 2*GR slots takes one
+// barrier per GR tiles (GR tiles computed on while the next GR are in flight).
 //
 // Layouts (v_mfma_f32_32x32x16_bf16, C[m][n] with lane = n):
 //   dkdv: S = Q K^T and dP = dO V^T put one KEY per lane, so P and dS are
@@ -38,8 +39,6 @@
 namespace fa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 
 #if FA_STATS
 __device__ unsigned long long g_bwd_stats[kStatCount];
@@ -74,31 +73,35 @@ __device__ __forceinline__ u32x4 load_row16(const uint16_t *base, int64_t row, i
 // ---------------------------------------------------------------------------
 // dK, dV: key-major.
 // ---------------------------------------------------------------------------
-template <int D, int BR_, int ST_, int KB_>
+template <int D, int BR_, int GR_, int KB_, int W_>
 struct DkdvCfg {
+    static constexpr int W = W_;                   // waves per workgroup
     static constexpr int BR = BR_;                 // queries per tile
     static constexpr int QB = BR / 32;             // 32-query blocks per tile
     static constexpr int KB = KB_;                 // 32-key blocks per wave
-    static constexpr int KEYS = 32 * KB * kWaves;  // keys per workgroup
+    static constexpr int KEYS = 32 * KB * W;       // keys per workgroup
     static constexpr int CH = D / 8, ROWB = D * 2;
     static constexpr int TILEB = BR * ROWB;        // one Q or dO tile
     static constexpr int VECB = 256;               // one L2 or D slice (64 lanes x 4 B)
     static constexpr int STAGEB = 2 * TILEB + 2 * VECB;
-    static constexpr int ST = ST_;
-    static constexpr int IPW = TILEB / 1024 / kWaves;
+    static constexpr int GR = GR_;                 // query tiles per LDS barrier
+    static constexpr int ST = 2 * GR;              // ring slots: GR in use, GR in flight
+    static constexpr int IPW = TILEB / 1024 / W;
     static constexpr int RPI = 1024 / ROWB;
-    static_assert(IPW >= 1 && BR <= 64 && ST >= 2 && ST <= 3, "dkdv tile");
+    static_assert(IPW >= 1 && IPW * W * 1024 == TILEB && BR <= 64, "dkdv tile");
+    static_assert(W == 4 || W == 8, "4 or 8 waves");
 };
 
-template <int D, int BR, int ST, int KB, bool CAUSAL>
-__global__ __launch_bounds__(kThreads)
+template <int D, int BR, int GR, int KB, int W, bool CAUSAL>
+__global__ __launch_bounds__(W * 64)
 __attribute__((amdgpu_waves_per_eu(D == 64 && KB == 1 ? 2 : 1, KB == 1 ? 2 : 1)))
 void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                      const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
                      const float *__restrict__ L2, const float *__restrict__ Dv,
                      uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int64_t Nq, int64_t Nk,
                      int64_t qoff, int nkt, uint32_t group, float scale, float c) {
-    using T = DkdvCfg<D, BR, ST, KB>;
+    using T = DkdvCfg<D, BR, GR, KB, W>;
+    constexpr int ST = T::ST;
     constexpr int QB = T::QB, ROWB = T::ROWB;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * T::STAGEB];
 
@@ -291,21 +294,22 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     const int nqt = (int)((Nq + BR - 1) / BR);
     const int it0 = CAUSAL ? (int)(k0 - qoff > 0 ? (k0 - qoff) / BR : 0) : 0;
 #pragma unroll
-    for (int t = 0; t < ST - 1; ++t)
+    for (int t = 0; t < GR; ++t)
         if (it0 + t < nqt) issue(it0 + t, t);
 
     for (int it = it0; it < nqt; ++it) {
         const int idx = it - it0;
-        if (ST == 3 && it + 1 < nqt) {
-            if (wave < 2)
-                wait_vm<(ST == 3 ? 2 * T::IPW + 1 : 0)>();
-            else
-                wait_vm<(ST == 3 ? 2 * T::IPW : 0)>();
-        } else {
+        // one barrier per GR query tiles: tiles idx .. idx+GR-1 (issued at the
+        // previous barrier, the only loads in flight) have landed and become
+        // visible, the slots of tiles idx-GR .. idx-1 are free, and tiles
+        // idx+GR .. idx+2GR-1 are issued into them
+        if (idx % GR == 0) {
             wait_vm<0>();
+            lds_barrier();
+#pragma unroll
+            for (int t = GR; t < 2 * GR; ++t)
+                if (it + t < nqt) issue(it + t, (idx + t) % ST);
         }
-        lds_barrier();
-        if (it + ST - 1 < nqt) issue(it + ST - 1, (idx + ST - 1) % ST);
         const int64_t q0 = (int64_t)it * BR;
         const int64_t q_last = (q0 + BR < Nq ? q0 + BR : Nq) - 1;  // last real query of the tile
         const bool active = kw0 < Nk && (!CAUSAL || q_last + qoff >= kw0);
@@ -354,27 +358,31 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
 // ---------------------------------------------------------------------------
 // dQ: query-major.
 // ---------------------------------------------------------------------------
-template <int D, int BC_, int ST_>
+template <int D, int BC_, int GR_, int W_>
 struct DqCfg {
-    static constexpr int BR = 32 * kWaves;          // queries per workgroup
+    static constexpr int W = W_;                    // waves per workgroup
+    static constexpr int BR = 32 * W;               // queries per workgroup
     static constexpr int BC = BC_;                  // keys per tile
     static constexpr int CH = D / 8, ROWB = D * 2;
     static constexpr int TILEB = BC * ROWB;
-    static constexpr int ST = ST_;
-    static constexpr int IPW = TILEB / 1024 / kWaves;
+    static constexpr int GR = GR_;                  // key tiles per LDS barrier
+    static constexpr int ST = 2 * GR;               // ring slots: GR in use, GR in flight
+    static constexpr int IPW = TILEB / 1024 / W;
     static constexpr int RPI = 1024 / ROWB;
-    static_assert(IPW >= 1 && ST >= 2 && ST <= 3, "dq tile");
+    static_assert(IPW >= 1 && IPW * W * 1024 == TILEB, "dq tile");
+    static_assert(W == 4 || W == 8, "4 or 8 waves");
 };
 
-template <int D, int BC, int ST, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, int BC, int GR, int W, bool CAUSAL>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                    const uint16_t *__restrict__ V, const uint16_t *__restrict__ O,
                    const uint16_t *__restrict__ dO, const float *__restrict__ L,
                    float *__restrict__ L2, float *__restrict__ Dv,
                    uint16_t *__restrict__ dQ, int64_t Nq, int64_t Nk, int64_t qoff, int nqt,
                    uint32_t group, float scale, float c) {
-    using T = DqCfg<D, BC, ST>;
+    using T = DqCfg<D, BC, GR, W>;
+    constexpr int ST = T::ST;
     constexpr int ROWB = T::ROWB;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * 2 * T::TILEB];
 
@@ -532,15 +540,16 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
             }
         }
     };
-    // ring step j: tile j has landed and is visible to every wave; the slot
-    // read in step j-1 is refilled
+    // ring step j: tile j has landed and is visible to every wave (a barrier
+    // every GR tiles publishes the next GR tiles and refills the slots of the
+    // previous GR)
     auto ring = [&](int64_t j) {
-        if (ST == 3 && j + 1 < nkt)
-            wait_vm<(ST == 3 ? 2 * T::IPW : 0)>();
-        else
-            wait_vm<0>();
+        if (j % GR != 0) return;  // one barrier per GR tiles, as in the dK/dV pass
+        wait_vm<0>();
         lds_barrier();
-        if (j + ST - 1 < nkt) issue(j + ST - 1, (int)((j + ST - 1) % ST));
+#pragma unroll
+        for (int t = GR; t < 2 * GR; ++t)
+            if (j + t < nkt) issue(j + t, (int)((j + t) % ST));
     };
     // leading tiles with every key visible to every query of this wave
     int64_t nfull = 0;
@@ -551,7 +560,7 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     }
 
 #pragma unroll
-    for (int t = 0; t < ST - 1; ++t)
+    for (int t = 0; t < GR; ++t)
         if (t < nkt) issue(t, t);
     int64_t j = 0;
     for (; j < nfull; ++j) {
@@ -585,9 +594,20 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 // Tile configurations (chosen by measurement on MI355X).
 #ifndef FA_BWD_DKDV_BR64
 #define FA_BWD_DKDV_BR64 64
-#define FA_BWD_DKDV_ST64 2
 #define FA_BWD_DQ_BC64 128
-#define FA_BWD_DQ_ST64 2
+#endif
+// d = 64 dK/dV pass: eight waves (one workgroup per CU, one Q/dO ring feeding
+// both waves of each SIMD) and one barrier per four query tiles, measured 4 %
+// faster per backward than four waves and a barrier per tile.  The dQ pass
+// keeps four waves (with eight the compiler spills) and, since two of its
+// workgroups share a CU's LDS, a barrier per key tile.
+#ifndef FA_BWD_W_DKDV64  // waves per workgroup, d = 64
+#define FA_BWD_W_DKDV64 8
+#define FA_BWD_W_DQ64 4
+#endif
+#ifndef FA_BWD_GR_DKDV64  // tiles per LDS barrier, d = 64
+#define FA_BWD_GR_DKDV64 4
+#define FA_BWD_GR_DQ64 1
 #endif
 #ifndef FA_BWD_DKDV_KB64  // 32-key blocks per wave in the dK/dV pass, d = 64
 #define FA_BWD_DKDV_KB64 1
@@ -603,29 +623,41 @@ struct DkdvChoice {
     // than 256 registers.
     static constexpr int KB = D == 64 ? FA_BWD_DKDV_KB64 : 1;
     static constexpr int BR = KB == 2 ? 32 : (D == 64 && CAUSAL ? FA_BWD_DKDV_BR64 : 32);
-    static constexpr int ST = D == 64 ? FA_BWD_DKDV_ST64 : 2;
+    // d = 128 needs more than 256 registers (one wave per SIMD): four waves;
+    // so does a 32-query tile, whose 4 KiB do not split over eight waves
+    static constexpr int W = D == 64 && BR == 64 ? FA_BWD_W_DKDV64 : 4;
+    static constexpr int GR = D == 64 ? FA_BWD_GR_DKDV64 : 1;
+    using Cfg = DkdvCfg<D, BR, GR, KB, W>;
+};
+
+template <int D>
+struct DqChoice {
+    static constexpr int BC = D == 64 ? FA_BWD_DQ_BC64 : 32;
+    static constexpr int W = D == 64 ? FA_BWD_W_DQ64 : 4;
+    static constexpr int GR = D == 64 ? FA_BWD_GR_DQ64 : 1;
+    using Cfg = DqCfg<D, BC, GR, W>;
 };
 
 template <int D, bool CAUSAL>
 hipError_t launch_main(const BwdArgs &a, hipStream_t s) {
     using C = DkdvChoice<D, CAUSAL>;
-    constexpr int BR = C::BR, ST = C::ST, KB = C::KB;
-    constexpr int BC = D == 64 ? FA_BWD_DQ_BC64 : 32;
-    constexpr int STQ = D == 64 ? FA_BWD_DQ_ST64 : 2;
+    using QC = DqChoice<D>;
     // the dQ pass first: it also writes D and L2, which the dK/dV pass reads
-    const int nqt = (int)((a.Nq + DqCfg<D, BC, STQ>::BR - 1) / DqCfg<D, BC, STQ>::BR);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BC, STQ, CAUSAL>), dim3((unsigned)(a.B * a.H * nqt)),
-                       dim3(kThreads), 0, s, (const uint16_t *)a.Q, (const uint16_t *)a.K,
-                       (const uint16_t *)a.V, (const uint16_t *)a.O, (const uint16_t *)a.dO, a.L,
-                       a.L2, a.D, (uint16_t *)a.dQ, a.Nq, a.Nk, a.q_start, nqt,
-                       tile_group(a.B * a.H), a.scale, a.scale * kLog2e);
+    const int nqt = (int)((a.Nq + QC::Cfg::BR - 1) / QC::Cfg::BR);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, QC::BC, QC::GR, QC::W, CAUSAL>),
+                       dim3((unsigned)(a.B * a.H * nqt)), dim3(QC::W * 64), 0, s,
+                       (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
+                       (const uint16_t *)a.O, (const uint16_t *)a.dO, a.L, a.L2, a.D,
+                       (uint16_t *)a.dQ, a.Nq, a.Nk, a.q_start, nqt, tile_group(a.B * a.H),
+                       a.scale, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int nkt = (int)((a.Nk + DkdvCfg<D, BR, ST, KB>::KEYS - 1) / DkdvCfg<D, BR, ST, KB>::KEYS);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BR, ST, KB, CAUSAL>), dim3((unsigned)(a.B * a.H * nkt)),
-                       dim3(kThreads), 0, s, (const uint16_t *)a.Q, (const uint16_t *)a.K,
-                       (const uint16_t *)a.V, (const uint16_t *)a.dO, a.L2, a.D, (uint16_t *)a.dK,
-                       (uint16_t *)a.dV, a.Nq, a.Nk, a.q_start, nkt, tile_group(a.B * a.H), a.scale,
+    const int nkt = (int)((a.Nk + C::Cfg::KEYS - 1) / C::Cfg::KEYS);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, C::BR, C::GR, C::KB, C::W, CAUSAL>),
+                       dim3((unsigned)(a.B * a.H * nkt)), dim3(C::W * 64), 0, s,
+                       (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
+                       (const uint16_t *)a.dO, a.L2, a.D, (uint16_t *)a.dK, (uint16_t *)a.dV,
+                       a.Nq, a.Nk, a.q_start, nkt, tile_group(a.B * a.H), a.scale,
                        a.scale * kLog2e);
     return hipGetLastError();
 }
