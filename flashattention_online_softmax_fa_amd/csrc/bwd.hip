@@ -358,6 +358,10 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
 // ---------------------------------------------------------------------------
 // dQ: query-major.
 // ---------------------------------------------------------------------------
+#ifndef FA_BWD_DQ_WPE  // waves per SIMD of the dQ pass
+#define FA_BWD_DQ_WPE 2
+#endif
+
 template <int D, int BC_, int GR_, int W_>
 struct DqCfg {
     static constexpr int W = W_;                    // waves per workgroup
@@ -374,7 +378,7 @@ struct DqCfg {
 };
 
 template <int D, int BC, int GR, int W, bool CAUSAL>
-__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(D == 64 ? FA_BWD_DQ_WPE : 2, D == 64 ? FA_BWD_DQ_WPE : 2)))
 void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                    const uint16_t *__restrict__ V, const uint16_t *__restrict__ O,
                    const uint16_t *__restrict__ dO, const float *__restrict__ L,
