@@ -613,6 +613,10 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 #define FA_BWD_GR_DKDV64 4
 #define FA_BWD_GR_DQ64 1
 #endif
+#ifndef FA_BWD_GR_DKDV128  // tiles per LDS barrier, d = 128 (one workgroup of four waves per CU)
+#define FA_BWD_GR_DKDV128 1
+#define FA_BWD_GR_DQ128 1
+#endif
 #ifndef FA_BWD_DKDV_KB64  // 32-key blocks per wave in the dK/dV pass, d = 64
 #define FA_BWD_DKDV_KB64 1
 #endif
@@ -630,7 +634,7 @@ struct DkdvChoice {
     // d = 128 needs more than 256 registers (one wave per SIMD): four waves;
     // so does a 32-query tile, whose 4 KiB do not split over eight waves
     static constexpr int W = D == 64 && BR == 64 ? FA_BWD_W_DKDV64 : 4;
-    static constexpr int GR = D == 64 ? FA_BWD_GR_DKDV64 : 1;
+    static constexpr int GR = D == 64 ? FA_BWD_GR_DKDV64 : FA_BWD_GR_DKDV128;
     using Cfg = DkdvCfg<D, BR, GR, KB, W>;
 };
 
@@ -638,7 +642,7 @@ template <int D>
 struct DqChoice {
     static constexpr int BC = D == 64 ? FA_BWD_DQ_BC64 : 32;
     static constexpr int W = D == 64 ? FA_BWD_W_DQ64 : 4;
-    static constexpr int GR = D == 64 ? FA_BWD_GR_DQ64 : 1;
+    static constexpr int GR = D == 64 ? FA_BWD_GR_DQ64 : FA_BWD_GR_DQ128;
     using Cfg = DqCfg<D, BC, GR, W>;
 };
 
