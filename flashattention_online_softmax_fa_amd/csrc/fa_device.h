@@ -209,6 +209,13 @@ __device__ __forceinline__ TileId tile_order(uint32_t bid, uint32_t heads, uint3
 // measured slower in every pass (forward 562 vs 545 us, backward 297 vs
 // 274 us): the balance of the launch matters more than the re-reads, which
 // use HBM bandwidth the matrix-core-bound kernels leave idle.
-inline uint32_t tile_group(int64_t heads) { return (uint32_t)(heads % 8 == 0 ? heads / 8 : heads); }
+#ifndef FA_TILE_GROUP  // heads per group (0: every head an XCD takes)
+#define FA_TILE_GROUP 0
+#endif
+inline uint32_t tile_group(int64_t heads) {
+    const int64_t per_xcd = heads % 8 == 0 ? heads / 8 : heads;
+    if (FA_TILE_GROUP > 0 && per_xcd % FA_TILE_GROUP == 0) return (uint32_t)FA_TILE_GROUP;
+    return (uint32_t)per_xcd;
+}
 
 }  // namespace fa
