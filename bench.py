@@ -246,8 +246,8 @@ def copy_calibration(torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(every (batch, head) is independent, see DESIGN.md for how it would shard)",
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported (every "
+              "(batch, head) is independent, so B*H would split over GPUs with no communication)",
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -223,3 +223,14 @@ def test_stats_tile_shapes():
     assert dbg.fa_stats_tile(4, FA_BF16, 64, 0, ctypes.byref(r), ctypes.byref(c)) == \
         FA_ERR_INVALID_ARG
     assert dbg.fa_stats_tile(0, FA_BF16, 64, 0, None, ctypes.byref(c)) == FA_ERR_INVALID_ARG
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: any other --gpus exits with status 2 and a
+    message, before touching the GPU."""
+    import subprocess
+    import sys as _sys
+    r = subprocess.run([_sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
