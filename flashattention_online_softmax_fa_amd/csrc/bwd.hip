@@ -362,10 +362,12 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
 #define FA_BWD_DQ_WPE 2
 #endif
 
-template <int D, int BC_, int GR_, int W_>
+template <int D, int BC_, int GR_, int W_, int QB_>
 struct DqCfg {
     static constexpr int W = W_;                    // waves per workgroup
-    static constexpr int BR = 32 * W;               // queries per workgroup
+    static constexpr int QB = QB_;                  // 32-query blocks per wave
+    static constexpr int QW = 32 * QB;              // queries per wave
+    static constexpr int BR = QW * W;               // queries per workgroup
     static constexpr int BC = BC_;                  // keys per tile
     static constexpr int CH = D / 8, ROWB = D * 2;
     static constexpr int TILEB = BC * ROWB;
@@ -377,7 +379,7 @@ struct DqCfg {
     static_assert(W == 4 || W == 8, "4 or 8 waves");
 };
 
-template <int D, int BC, int GR, int W, bool CAUSAL>
+template <int D, int BC, int GR, int W, int QB, bool CAUSAL>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(D == 64 ? FA_BWD_DQ_WPE : 2, D == 64 ? FA_BWD_DQ_WPE : 2)))
 void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                    const uint16_t *__restrict__ V, const uint16_t *__restrict__ O,
@@ -385,7 +387,7 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
                    float *__restrict__ L2, float *__restrict__ Dv,
                    uint16_t *__restrict__ dQ, int64_t Nq, int64_t Nk, int64_t qoff, int nqt,
                    uint32_t group, float scale, float c) {
-    using T = DqCfg<D, BC, GR, W>;
+    using T = DqCfg<D, BC, GR, W, QB>;
     constexpr int ST = T::ST;
     constexpr int ROWB = T::ROWB;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * 2 * T::TILEB];
@@ -397,8 +399,7 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     const int64_t bh = tid_.head;
     const int qt = CAUSAL ? nqt - 1 - (int)tid_.rank : (int)tid_.rank;  // causal: late queries see the most keys
     const int64_t q0 = (int64_t)qt * T::BR;
-    const int64_t qw0 = q0 + wave * 32;
-    const int64_t qrow = qw0 + lr;
+    const int64_t qw0 = q0 + wave * T::QW;  // query block qb of this wave: qw0 + 32qb + lane%32
     const uint16_t *Kh = K + bh * Nk * D;
     const uint16_t *Vh = V + bh * Nk * D;
 
@@ -408,38 +409,45 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
         const int64_t lim = (qlast + qoff) / BC + 1;
         nkt = nkt < lim ? nkt : lim;
     }
-    const int64_t qw_last = (qw0 + 31 < Nq - 1) ? qw0 + 31 : Nq - 1;
+    const int64_t qw_last = (qw0 + T::QW - 1 < Nq - 1) ? qw0 + T::QW - 1 : Nq - 1;
 
-    // Q and dO of this lane's query: B operands of S^T = K Q^T and dP^T = V dO^T
-    bf16x8 qf[D / 16], of[D / 16];
+    // Q and dO of this lane's queries (one per 32-query block): B operands of
+    // S^T = K Q^T and dP^T = V dO^T; each K and V fragment read from LDS
+    // serves the QB blocks
+    bf16x8 qf[QB][D / 16], of[QB][D / 16];
+    float l2[QB], dq[QB];
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-        qf[ds] = __builtin_bit_cast(bf16x8, load_row16(Q + bh * Nq * D, qrow, Nq, D, ds * 2 + g));
-        of[ds] = __builtin_bit_cast(bf16x8, load_row16(dO + bh * Nq * D, qrow, Nq, D, ds * 2 + g));
-    }
-    // D = rowsum(dO * O) and L2 = L * log2(e) of this lane's query: the lane
-    // holds half of the row (chunks 2ds + g), lane ^ 32 the other half.  The
-    // dK/dV pass, launched after this one, reads both from the workspace.
-    const int64_t qc = qrow < Nq ? qrow : Nq - 1;
-    float dsum = 0.f;
+    for (int qb = 0; qb < QB; ++qb) {
+        const int64_t qrow = qw0 + 32 * qb + lr;
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-        const u32x4 o = load_row16(O + bh * Nq * D, qrow, Nq, D, ds * 2 + g);
-        const u32x4 w = __builtin_bit_cast(u32x4, of[ds]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            dsum = fmaf(bf16_lo(o[e]), bf16_lo(w[e]), dsum);
-            dsum = fmaf(bf16_hi(o[e]), bf16_hi(w[e]), dsum);
+        for (int ds = 0; ds < D / 16; ++ds) {
+            qf[qb][ds] = __builtin_bit_cast(bf16x8, load_row16(Q + bh * Nq * D, qrow, Nq, D, ds * 2 + g));
+            of[qb][ds] = __builtin_bit_cast(bf16x8, load_row16(dO + bh * Nq * D, qrow, Nq, D, ds * 2 + g));
         }
+        // D = rowsum(dO * O) and L2 = L * log2(e) of this query: the lane holds
+        // half of the row (chunks 2ds + g), lane ^ 32 the other half.  The
+        // dK/dV pass, launched after this one, reads both from the workspace.
+        const int64_t qc = qrow < Nq ? qrow : Nq - 1;
+        float dsum = 0.f;
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) {
+            const u32x4 o = load_row16(O + bh * Nq * D, qrow, Nq, D, ds * 2 + g);
+            const u32x4 w = __builtin_bit_cast(u32x4, of[qb][ds]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dsum = fmaf(bf16_lo(o[e]), bf16_lo(w[e]), dsum);
+                dsum = fmaf(bf16_hi(o[e]), bf16_hi(w[e]), dsum);
+            }
+        }
+        dsum += __shfl_xor(dsum, 32);
+        const float lrow = L[bh * Nq + qc];
+        if (g == 0 && qrow < Nq) {
+            L2[bh * Nq + qc] = lrow * kLog2e;
+            Dv[bh * Nq + qc] = dsum;
+        }
+        l2[qb] = qrow < Nq ? lrow * kLog2e : INFINITY;  // padded row: P = 0
+        dq[qb] = qrow < Nq ? dsum : 0.f;
     }
-    dsum += __shfl_xor(dsum, 32);
-    const float lrow = L[bh * Nq + qc];
-    if (g == 0 && qrow < Nq) {
-        L2[bh * Nq + qc] = lrow * kLog2e;
-        Dv[bh * Nq + qc] = dsum;
-    }
-    const float l2 = qrow < Nq ? lrow * kLog2e : INFINITY;  // padded row: P = 0
-    const float dq = qrow < Nq ? dsum : 0.f;
 
     auto ld_row = [&](int u) { return (wave * T::IPW + u) * T::RPI + lane / T::CH; };
     uint32_t ld_off[T::IPW];  // byte offset of this lane's load within a tile
@@ -476,11 +484,13 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 #pragma unroll
     for (int b = 0; b < D / 32; ++b) toff[b] = tr_off<ROWB>(lane, b, 0);
 
-    f32x16 acc[D / 32];
+    f32x16 acc[QB][D / 32];
 #pragma unroll
-    for (int b = 0; b < D / 32; ++b)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[qb][b][r] = 0.f;
 #if FA_STATS
     uint32_t st_tiles = 0;
 #endif
@@ -496,51 +506,66 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 #endif
         const uint8_t *vt = kt + T::TILEB;
 
-        // ---- S^T = K Q^T, dP^T = V dO^T (lane: query lr; register r: key
-        //      8*(r/4) + 4g + r%4 of the 32-key block)
-        f32x16 sacc[BC / 32], pacc[BC / 32];
+        // The tile is walked one 32-key block at a time (scores, vector work,
+        // dQ products), so that only one block's scores are live.
 #pragma unroll
         for (int kb = 0; kb < BC / 32; ++kb) {
+            // ---- S^T = K Q^T, dP^T = V dO^T (lane: query lr of block qb;
+            //      register r: key 8*(r/4) + 4g + r%4 of the 32-key block)
+            f32x16 sacc[QB], pacc[QB];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                sacc[kb][r] = 0.f;
-                pacc[kb][r] = 0.f;
-            }
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    sacc[qb][r] = 0.f;
+                    pacc[qb][r] = 0.f;
+                }
 #pragma unroll
             for (int ds = 0; ds < D / 16; ++ds) {
                 const int off = kb * 32 * ROWB + koff[ds];
                 const bf16x8 ak = *(const bf16x8 *)(kt + off);
                 const bf16x8 av = *(const bf16x8 *)(vt + off);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[ds], sacc[kb], 0, 0, 0);
-                pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[ds], pacc[kb], 0, 0, 0);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[qb][ds], sacc[qb], 0, 0, 0);
+                    pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[qb][ds], pacc[qb], 0, 0, 0);
+                }
             }
-        }
-        // ---- P = exp2(S c - L2), dS = P (dP - D), both per lane; masked tiles
-        //      zero the keys past Nk and after the query
-        int lim = BC;
-        if (MASKED) {
-            int64_t lim64 = Nk - 1 - kv0;  // last visible key offset
-            if (CAUSAL && qrow + qoff - kv0 < lim64) lim64 = qrow + qoff - kv0;
-            lim = (int)(lim64 < -1 ? -1 : (lim64 > BC ? BC : lim64)) - 4 * g;
-        }
+            // ---- P = exp2(S c - L2), dS = P (dP - D), both per lane; masked
+            //      tiles zero the keys past Nk and after the query
 #pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb)
+            for (int qb = 0; qb < QB; ++qb) {
+                int lim = 32;
+                if (MASKED) {
+                    const int64_t qrow = qw0 + 32 * qb + lr;
+                    const int64_t kb0 = kv0 + kb * 32;
+                    int64_t lim64 = Nk - 1 - kb0;  // last visible key offset in the block
+                    if (CAUSAL && qrow + qoff - kb0 < lim64) lim64 = qrow + qoff - kb0;
+                    lim = (int)(lim64 < -1 ? -1 : (lim64 > 32 ? 32 : lim64)) - 4 * g;
+                }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = fast_exp2(fmaf(sacc[kb][r], c, -l2));
-                if (MASKED && kb * 32 + 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
-                pacc[kb][r] = p * (pacc[kb][r] - dq);
+                for (int r = 0; r < 16; ++r) {
+                    float p = fast_exp2(fmaf(sacc[qb][r], c, -l2[qb]));
+                    if (MASKED && 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
+                    pacc[qb][r] = p * (pacc[qb][r] - dq[qb]);
+                }
             }
-        // ---- dQ^T += K^T dS^T.  B operand (k-step ks of 16 keys) = registers
-        //      8h..8h+7 of block ks/2: k-slot (g, e) is key 8*(e/4) + 4g + e%4 of
-        //      the step; K^T is read transposed in the same slot order.
+            // ---- dQ^T += K^T dS^T.  B operand (k-step h of 16 keys) = registers
+            //      8h..8h+7: k-slot (g, e) is key 8*(e/4) + 4g + e%4 of the step;
+            //      K^T is read transposed in the same slot order and serves the
+            //      QB blocks.
 #pragma unroll
-        for (int ks = 0; ks < BC / 16; ++ks) {
-            const bf16x8 sb = pack8(pacc[ks >> 1], 8 * (ks & 1));
+            for (int h = 0; h < 2; ++h) {
+                bf16x8 sb[QB];
 #pragma unroll
-            for (int b = 0; b < D / 32; ++b) {
-                const bf16x8 a = tr_pair<ROWB>(kt + ks * 16 * ROWB, toff[b]);
-                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb, acc[b], 0, 0, 0);
+                for (int qb = 0; qb < QB; ++qb) sb[qb] = pack8(pacc[qb], 8 * h);
+#pragma unroll
+                for (int b = 0; b < D / 32; ++b) {
+                    const bf16x8 a = tr_pair<ROWB>(kt + (2 * kb + h) * 16 * ROWB, toff[b]);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        acc[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[qb], acc[qb][b], 0, 0, 0);
+                }
             }
         }
     };
@@ -580,18 +605,23 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 #if FA_STATS
     if (lane == 0 && qw0 < Nq) atomicAdd(&g_bwd_stats[4], (unsigned long long)st_tiles);
 #endif
-    // ---- epilogue: dQ = scale * acc (lane: query lr; register r: column
-    //      32b + 8*(r/4) + 4g + r%4)
-    if (qrow < Nq) {
-        uint16_t *row = dQ + (bh * Nq + qrow) * D;
+    // ---- epilogue: dQ = scale * acc (lane: query lr of block qb; register r:
+    //      column 32b + 8*(r/4) + 4g + r%4)
 #pragma unroll
-        for (int b = 0; b < D / 32; ++b)
+    for (int qb = 0; qb < QB; ++qb) {
+        const int64_t qrow = qw0 + 32 * qb + lr;
+        if (qrow < Nq) {
+            uint16_t *row = dQ + (bh * Nq + qrow) * D;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const u32x2 w = {pack_bf16x2(scale * acc[b][4 * t], scale * acc[b][4 * t + 1]),
-                                 pack_bf16x2(scale * acc[b][4 * t + 2], scale * acc[b][4 * t + 3])};
-                *(u32x2 *)(row + b * 32 + 8 * t + 4 * g) = w;
-            }
+            for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const f32x16 &a = acc[qb][b];
+                    const u32x2 w = {pack_bf16x2(scale * a[4 * t], scale * a[4 * t + 1]),
+                                     pack_bf16x2(scale * a[4 * t + 2], scale * a[4 * t + 3])};
+                    *(u32x2 *)(row + b * 32 + 8 * t + 4 * g) = w;
+                }
+        }
     }
 }
 
@@ -600,18 +630,22 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 #define FA_BWD_DKDV_BR64 64
 #define FA_BWD_DQ_BC64 128
 #endif
-// d = 64 dK/dV pass: eight waves (one workgroup per CU, one Q/dO ring feeding
-// both waves of each SIMD) and one barrier per four query tiles, measured 4 %
-// faster per backward than four waves and a barrier per tile.  The dQ pass
-// keeps four waves (with eight the compiler spills) and, since two of its
-// workgroups share a CU's LDS, a barrier per key tile.
+// d = 64: both passes on eight waves (one workgroup per CU, one ring feeding
+// both waves of each SIMD), the dK/dV pass with one barrier per four query
+// tiles and the dQ pass with one per two key tiles: 4 % and 2 % faster per
+// backward than four waves and a barrier per tile.  (The dQ pass fits eight
+// waves because it walks each key tile one 32-key block at a time.)  Two
+// query blocks per dQ wave halve its LDS reads but measured 20 % slower.
 #ifndef FA_BWD_W_DKDV64  // waves per workgroup, d = 64
 #define FA_BWD_W_DKDV64 8
-#define FA_BWD_W_DQ64 4
+#define FA_BWD_W_DQ64 8
+#endif
+#ifndef FA_BWD_DQ_QB64  // 32-query blocks per wave of the dQ pass, d = 64
+#define FA_BWD_DQ_QB64 1
 #endif
 #ifndef FA_BWD_GR_DKDV64  // tiles per LDS barrier, d = 64
 #define FA_BWD_GR_DKDV64 4
-#define FA_BWD_GR_DQ64 1
+#define FA_BWD_GR_DQ64 2
 #endif
 #ifndef FA_BWD_GR_DKDV128  // tiles per LDS barrier, d = 128 (one workgroup of four waves per CU)
 #define FA_BWD_GR_DKDV128 1
@@ -643,7 +677,8 @@ struct DqChoice {
     static constexpr int BC = D == 64 ? FA_BWD_DQ_BC64 : 32;
     static constexpr int W = D == 64 ? FA_BWD_W_DQ64 : 4;
     static constexpr int GR = D == 64 ? FA_BWD_GR_DQ64 : FA_BWD_GR_DQ128;
-    using Cfg = DqCfg<D, BC, GR, W>;
+    static constexpr int QB = D == 64 ? FA_BWD_DQ_QB64 : 1;
+    using Cfg = DqCfg<D, BC, GR, W, QB>;
 };
 
 template <int D, bool CAUSAL>
@@ -652,7 +687,7 @@ hipError_t launch_main(const BwdArgs &a, hipStream_t s) {
     using QC = DqChoice<D>;
     // the dQ pass first: it also writes D and L2, which the dK/dV pass reads
     const int nqt = (int)((a.Nq + QC::Cfg::BR - 1) / QC::Cfg::BR);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, QC::BC, QC::GR, QC::W, CAUSAL>),
+    hipLaunchKernelGGL((bwd_dq_kernel<D, QC::BC, QC::GR, QC::W, QC::QB, CAUSAL>),
                        dim3((unsigned)(a.B * a.H * nqt)), dim3(QC::W * 64), 0, s,
                        (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
                        (const uint16_t *)a.O, (const uint16_t *)a.dO, a.L, a.L2, a.D,
@@ -685,7 +720,7 @@ void bwd_bf16_tiles(int64_t d, int causal, int64_t *kv_rows, int64_t *kv_cols, i
                     int64_t *q_cols) {
     *kv_rows = d == 64 ? (causal ? 32 * DkdvChoice<64, true>::KB : 32 * DkdvChoice<64, false>::KB) : 32;
     *kv_cols = d == 64 ? (causal ? DkdvChoice<64, true>::BR : DkdvChoice<64, false>::BR) : 32;
-    *q_rows = 32;
+    *q_rows = d == 64 ? 32 * FA_BWD_DQ_QB64 : 32;
     *q_cols = d == 64 ? FA_BWD_DQ_BC64 : 32;
 }
 #endif
