@@ -11,6 +11,13 @@ on a bounded sample on this host) and ``parts``: the causal d=128 prefill
 forward, the causal backward (10*B*H*N^2*d/2 per step) and split-KV decoding
 (GB/s of K, V, Q, O and L), each timed the same way.
 
+After each workload is timed it keeps running back to back for --clock-s
+seconds while a thread reads the shader clock the driver reports
+(``sclk_mhz``, the median of the samples; ``sustained_ms``, the time per step
+over the same interval): under these loads the clock stays below the 2.4 GHz
+the published matrix peak assumes, and ``frac_at_sclk`` is the sustained rate
+over the peak scaled to the clock measured.
+
 --workload selects another workload as the primary one.  --copy-calibration
 runs a plain device copy of known size (for scaling rocprofv3 FETCH_SIZE and
 WRITE_SIZE counters to bytes).  Only one GPU is used; --gpus N > 1 exits.
@@ -29,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_SCLK_MHZ = 2400.0      # the engine clock that peak is quoted at
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
@@ -56,6 +64,8 @@ def parse():
     p.add_argument("--n-split", type=int, default=None, help="decode: splits (default best)")
     p.add_argument("--no-parts", action="store_true", help="time only the primary workload")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    p.add_argument("--clock-s", type=float, default=1.5,
+                   help="seconds of extra steps per workload while the clock is sampled (0: off)")
     p.add_argument("--copy-calibration", action="store_true")
     return p.parse_args()
 
@@ -150,6 +160,86 @@ def measure(run, torch, steps, warmup, settle_s):
         run["cfg"]["n_split"] = best[1]
         return best[0]
     return timed(torch, run["step"], steps, warmup, settle_s)
+
+
+def sclk_path(torch):
+    """The amdgpu pp_dpm_sclk file of cuda:0's PCI function, or None."""
+    try:
+        p = torch.cuda.get_device_properties(0)
+        path = (f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:"
+                f"{p.pci_device_id:02x}.0/pp_dpm_sclk")
+    except (AttributeError, RuntimeError):
+        return None
+    return path if os.path.exists(path) else None
+
+
+def read_sclk(path):
+    """Current shader clock in MHz: the pp_dpm_sclk line marked '*'."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    return float(line.split(":")[1].strip().split("Mhz")[0])
+    except (OSError, ValueError, IndexError):
+        pass
+    return None
+
+
+def sample_clock(torch, step, seconds):
+    """Run `step` back to back for `seconds` while a second thread reads the
+    shader clock every 20 ms (after the first 0.3 s).  Returns (median clock
+    in MHz, ms per step over the same interval), or None when the driver file
+    is not readable or sampling is off."""
+    import threading
+    path = sclk_path(torch)
+    if path is None or seconds <= 0:
+        return None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        t0 = time.perf_counter()
+        while not stop.wait(0.02):
+            if time.perf_counter() - t0 > 0.3:
+                v = read_sclk(path)
+                if v:
+                    samples.append(v)
+    stream = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    a.record(stream)
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            step()
+        n += 16
+        torch.cuda.synchronize()
+    b.record(stream)
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    samples.sort()
+    return samples[len(samples) // 2], a.elapsed_time(b) / n
+
+
+def add_clock(rf, run, sampled):
+    """Clock fields of a roofline entry: the median shader clock while the
+    workload ran back to back, the rate over that interval, and for a
+    matrix-bound kernel the peak scaled to that clock and the fraction of it."""
+    if sampled is None:
+        rf["sclk_mhz"] = None
+        return
+    sclk, ms = sampled
+    rf["sclk_mhz"] = sclk
+    rf["sustained_ms"] = round(ms, 5)
+    if rf["bound"] == "mfma":
+        p = rf["peak"] * sclk / PEAK_SCLK_MHZ
+        rf["peak_at_sclk"] = round(p, 1)
+        rf["frac_at_sclk"] = round(rate(run, ms) / p, 4)
 
 
 def rate(run, ms):
@@ -268,6 +358,7 @@ def main():
         "config": run["cfg"],
         "roofline": roofline(run, ms, args.workload),
     }
+    add_clock(line["roofline"], run, sample_clock(torch, run["step"], args.clock_s))
     if run["kernel"] == "fwd_bf16_kernel":
         line["roofline"]["io_flash"] = io_model(run, fa)
     if "partial_bytes" in run:
@@ -287,9 +378,12 @@ def main():
             steps = max(3, args.steps // 2) if name == "decode_d128" else args.steps
             pms = measure(r, torch, steps, min(args.warmup, 3), args.settle)
             rf = roofline(r, pms, name)
+            add_clock(rf, r, sample_clock(torch, r["step"], args.clock_s))
             parts[name] = {"ms": round(pms, 5), "value": round(rate(r, pms), 3),
                            "unit": rf["unit"], "frac": rf["frac"], "traffic": rf["traffic"],
-                           "config": r["cfg"]}
+                           "sclk_mhz": rf["sclk_mhz"], "config": r["cfg"]}
+            if "frac_at_sclk" in rf:
+                parts[name]["frac_at_sclk"] = rf["frac_at_sclk"]
             if r["kernel"] == "fwd_bf16_kernel":
                 parts[name]["io_flash"] = io_model(r, fa)
             if "partial_bytes" in r:

@@ -11,7 +11,8 @@ allocate the outputs with torch before calling them.
 torch provides device memory and streams only.  It is imported before
 libfa.so is loaded so that both use the one HIP runtime already in the
 process.  There is no fallback: if libfa.so is missing, importing this module
-raises ImportError.
+raises ImportError.  FA_LIBRARY, when set, names another build of the same
+sources to load instead (``build.py --variant``: other tile constants).
 """
 from __future__ import annotations
 
@@ -22,7 +23,7 @@ import os
 import torch
 
 _PKG_DIR = _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfa.so")
+LIB_PATH = os.environ.get("FA_LIBRARY") or os.path.join(_HERE, "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_F32, FA_BF16 = 0, 1

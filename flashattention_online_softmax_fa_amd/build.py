@@ -7,6 +7,12 @@ count events (include/fa_stats.h).  Run it as a script
 (``python flashattention_online_softmax_fa_amd/build.py``) or through
 ``__graft_entry__.build()``; importing the package itself needs the built
 library.
+
+``--variant NAME -DMACRO=VALUE ...`` builds ``variants/libfa_NAME.so`` from
+the same sources with other compile-time tile constants (the FA_FWD_*,
+FA_BWD_* and FA_TILE_GROUP macros of the kernels); setting FA_LIBRARY to its
+path makes the package load it in place of libfa.so, so that the tile-size
+choices can be timed and profiled against each other with the same scripts.
 """
 from __future__ import annotations
 
@@ -22,6 +28,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 SO = os.path.join(PKG, "libfa.so")
 STATS_SO = os.path.join(PKG, "libfa_stats.so")
+VARIANT_DIR = os.path.join(PKG, "variants")
 
 SOURCES = ["fa_api.hip", "fwd_f32.hip", "fwd_bf16.hip", "bwd.hip", "bwd_f32.hip", "decode.hip"]
 
@@ -87,6 +94,29 @@ def build(verbose: bool = False, stats: bool = True) -> str:
     return SO
 
 
+def build_variant(name: str, defines, verbose: bool = False) -> str:
+    """libfa.so built with extra -D definitions, as variants/libfa_<name>.so."""
+    if not name.replace("_", "").isalnum():
+        raise ValueError(f"variant name {name!r}: letters, digits and '_' only")
+    for d in defines:
+        if not d.startswith("-DFA_"):
+            raise ValueError(f"{d!r}: variants take -DFA_... definitions only")
+    objdir = os.path.join(OBJDIR, "variants", name)
+    os.makedirs(objdir, exist_ok=True)
+    os.makedirs(VARIANT_DIR, exist_ok=True)
+    jobs = [(src, objdir, list(defines)) for src in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, jobs))
+    so = os.path.join(VARIANT_DIR, f"libfa_{name}.so")
+    _link(objs, so)
+    if verbose:
+        print(f"built {so} ({' '.join(defines)})")
+    return so
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if len(sys.argv) > 2 and sys.argv[1] == "--variant":
+        build_variant(sys.argv[2], sys.argv[3:], verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

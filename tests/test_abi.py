@@ -234,3 +234,32 @@ def test_bench_refuses_several_gpus():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
+
+
+def test_bench_reads_shader_clock(tmp_path):
+    """The clock bench.py reports is the pp_dpm_sclk line the driver marks
+    as current, both at a DPM level and in deep sleep; the matrix peak is
+    scaled by it."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("0: 500Mhz\n1: 2247Mhz *\n")
+    assert bench.read_sclk(str(f)) == 2247.0
+    f.write_text("S: 103Mhz *\n0: 500Mhz\n1: 2400Mhz\n")
+    assert bench.read_sclk(str(f)) == 103.0
+    f.write_text("0: 500Mhz\n1: 2400Mhz\n")
+    assert bench.read_sclk(str(f)) is None
+    assert bench.read_sclk(str(tmp_path / "missing")) is None
+    run = {"work": 1e12, "unit": "TFLOP/s"}        # 1 TFLOP per step
+    rf = {"bound": "mfma", "peak": 2500.0}
+    bench.add_clock(rf, run, (2100.0, 1.0))       # 1 ms per step: 1000 TFLOP/s
+    assert rf["peak_at_sclk"] == 2187.5 and rf["frac_at_sclk"] == round(1000 / 2187.5, 4)
+    assert rf["sustained_ms"] == 1.0
+    rf = {"bound": "hbm", "peak": 8000.0}
+    bench.add_clock(rf, {"work": 7e9, "unit": "GB/s"}, (2100.0, 1.0))
+    assert rf["sclk_mhz"] == 2100.0 and "frac_at_sclk" not in rf
+    rf = {"bound": "mfma", "peak": 2500.0}
+    bench.add_clock(rf, run, None)
+    assert rf["sclk_mhz"] is None
