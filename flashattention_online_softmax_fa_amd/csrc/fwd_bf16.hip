@@ -24,6 +24,10 @@
 // sets.  Leading tiles that need no mask for any of the wave's rows run a
 // mask-free loop; the rest (the ragged end of the keys, the causal diagonal,
 // and the idle steps of waves whose rows end earlier) run a generic one.
+// Mask-free steps do not reduce the tile maximum before exponentiating: they
+// exponentiate against the reference maximum and raise it only when the
+// resulting sums show a score more than about 20 (base 2) above it, which
+// keeps the row-max reductions off the common path.
 //
 // LDS layout.  K and V tiles are row-major (one key per row, 16-byte chunks).
 // Chunks are XOR-swizzled per row (swz in fa_device.h) so that both access
@@ -62,6 +66,9 @@
 #endif
 #ifndef FA_FWD_WG128
 #define FA_FWD_WG128 8
+#endif
+#ifndef FA_FWD_LAZY  // 1: mask-free steps skip the tile maximum (see step())
+#define FA_FWD_LAZY 1
 #endif
 #ifndef FA_FWD_GR64  // key tiles per LDS barrier (the ring depth must be >= 2 * this + 1)
 #define FA_FWD_GR64 4
@@ -298,64 +305,54 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     // tile t (scores in cur), compute the scores of tile t+1 into nxt
     // meanwhile, and accumulate O with tile t's values.  `generic` steps mask
     // tile t+1 where needed and handle a wave's last tile.
-    auto step = [&](int t, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB], auto generic) {
-        constexpr bool GEN = decltype(generic)::value;
-        // ---- online softmax (base 2).  m is a reference maximum: it is raised
-        //      (and the accumulator rescaled) only when the tile maximum exceeds
-        //      it by more than kMargin, so exponents stay <= 2^kMargin and most
-        //      tiles skip the rescale.  O = acc / l and L = m + log2 l do not
-        //      depend on which reference is used.  The first tile always raises
-        //      it (every row sees key 0), so m is finite afterwards.
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            if (__any(mt[qb] > m[qb] + kMargin)) {
-                // the other half of the row is in lane ^ 32
-                const float mj = fmaxf(mt[qb], __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                                                        xaddr, __builtin_bit_cast(int, mt[qb]))));
-                const bool grow = mj > m[qb] + kMargin;  // same in both lanes of the row
-                const float m_new = grow ? mj : m[qb];
-                const float alpha = fast_exp2(m[qb] - m_new);  // 0 on the first tile, else <= 1
+    // raise the reference maximum of query block qb to the row maximum of the
+    // tile whose lane maxima are in mt[qb] where that exceeds it by more than
+    // kMargin, rescaling the row's accumulator and sum
+    auto raise = [&](int qb) {
+        // the other half of the row is in lane ^ 32
+        const float mj = fmaxf(mt[qb], __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                                xaddr, __builtin_bit_cast(int, mt[qb]))));
+        const bool grow = mj > m[qb] + kMargin;  // same in both lanes of the row
+        const float m_new = grow ? mj : m[qb];
+        const float alpha = fast_exp2(m[qb] - m_new);  // 0 on the first tile, else <= 1
 #if FA_STATS
-                if (grow && m[qb] > -INFINITY && g == 0 && qw0 + 32 * qb + lr < Nq) ++st_resc;
+        if (grow && m[qb] > -INFINITY && g == 0 && qw0 + 32 * qb + lr < Nq) ++st_resc;
 #endif
-                l0[qb] *= alpha;
-                l1[qb] *= alpha;
+        l0[qb] *= alpha;
+        l1[qb] *= alpha;
 #pragma unroll
-                for (int b = 0; b < D / 32; ++b)
+        for (int b = 0; b < D / 32; ++b)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[qb][b][r] *= alpha;
-                m[qb] = m_new;
+            for (int r = 0; r < 16; ++r) oacc[qb][b][r] *= alpha;
+        m[qb] = m_new;
+    };
+    // P^T of query block qb of the tile in cur as bf16 B operands (k-step ks
+    // uses registers 8h..8h+7 of block ks/2, so k-slot (g, e) is key
+    // 8*(e/4) + 4g + e%4 of the step); the probabilities are summed into s0, s1
+    auto probs = [&](int qb, const f32x16 (&cur)[QB][KB], bf16x8 (&pf)[QB][BC / 16], float &s0,
+                     float &s1) {
+#pragma unroll
+        for (int ks = 0; ks < BC / 16; ++ks) {
+            const int kb = ks >> 1, h = ks & 1;
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                p[e] = fast_exp2(POS_SCALE ? fmaf(cur[qb][kb][8 * h + e], c, -m[qb])
+                                           : cur[qb][kb][8 * h + e] - m[qb]);
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                s0 += p[e];
+                s1 += p[e + 1];
             }
+            const u32x4 w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                             pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+            pf[qb][ks] = __builtin_bit_cast(bf16x8, w);
         }
-        const bool next = GEN ? t + 1 < nkt_w : true;
-        if (!GEN || next) scores((t + 1) % S, nxt);
-
-        // ---- P^T as bf16 B operands: k-step ks uses registers 8h..8h+7 of block
-        //      ks/2, so k-slot (g, e) is key 8*(e/4) + 4g + e%4 of the step
-        bf16x8 pf[QB][BC / 16];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-            for (int ks = 0; ks < BC / 16; ++ks) {
-                const int kb = ks >> 1, h = ks & 1;
-                float p[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    p[e] = fast_exp2(POS_SCALE ? fmaf(cur[qb][kb][8 * h + e], c, -m[qb])
-                                               : cur[qb][kb][8 * h + e] - m[qb]);
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    l0[qb] += p[e];
-                    l1[qb] += p[e + 1];
-                }
-                const u32x4 w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-                pf[qb][ks] = __builtin_bit_cast(bf16x8, w);
-            }
-        }
-        // ---- O^T += V_t^T P^T; V^T read transposed in the same k-slot order and
-        //      shared by the QB query blocks
-        const uint8_t *vbase = smem + (t % S) * 2 * T::TILEB + T::TILEB;
+    };
+    // O^T += V_u^T P^T of tile u (P^T in pf); V^T read transposed in the same
+    // k-slot order and shared by the QB query blocks
+    auto pv = [&](int u, const bf16x8 (&pf)[QB][BC / 16]) {
+        const uint8_t *vbase = smem + (u % S) * 2 * T::TILEB + T::TILEB;
 #pragma unroll
         for (int ks = 0; ks < BC / 16; ++ks) {
 #pragma unroll
@@ -370,15 +367,66 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
                         __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][ks], oacc[qb][b], 0, 0, 0);
             }
         }
+    };
+    auto step = [&](int t, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB], auto generic) {
+        constexpr bool GEN = decltype(generic)::value;
+        // ---- online softmax (base 2).  m is a reference maximum: O = acc / l
+        //      and L = m + log2 l do not depend on which reference is used, so
+        //      it is raised (and the accumulator and sum rescaled) only when
+        //      the exponentials would otherwise grow large.  Generic steps
+        //      (with FA_FWD_LAZY = 0, every step) compare the tile maximum with
+        //      m + kMargin before exponentiating; mask-free steps skip the tile
+        //      maximum, exponentiate against m and check the sums afterwards.
+        constexpr bool LAZY = FA_FWD_LAZY && !GEN;
+        if constexpr (!LAZY) {
+            if constexpr (FA_FWD_LAZY) tile_max(cur);  // else computed by the previous step
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                if (__any(mt[qb] > m[qb] + kMargin)) raise(qb);
+        }
+        const bool next = GEN ? t + 1 < nkt_w : true;
+        if (!GEN || next) scores((t + 1) % S, nxt);
+
+        bf16x8 pf[QB][BC / 16];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            if constexpr (LAZY) {
+                // Exponents against the current reference.  Every probability
+                // is <= its lane's sums, so sums <= 2^24 keep P, O and l far
+                // from fp32 overflow; otherwise (an infinite or NaN sum
+                // included) raise the reference to the row maximum of the tile
+                // and exponentiate again.  Rare: it takes a score more than 20
+                // above the reference in base 2.
+                float s0 = 0.f, s1 = 0.f;
+                probs(qb, cur, pf, s0, s1);
+                if (__any(!(fmaxf(s0, s1) <= 0x1p24f))) {
+                    float v = -INFINITY;
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) v = fmaxf(v, cur[qb][kb][r]);
+                    mt[qb] = POS_SCALE ? v * c : v;
+                    raise(qb);
+                    s0 = 0.f;
+                    s1 = 0.f;
+                    probs(qb, cur, pf, s0, s1);
+                }
+                l0[qb] += s0;
+                l1[qb] += s1;
+            } else {
+                probs(qb, cur, pf, l0[qb], l1[qb]);
+            }
+        }
+        pv(t, pf);
         if (!GEN || next) {
             if (GEN && t + 1 >= nfull) mask(t + 1, nxt);
-            tile_max(nxt);
+            if (!FA_FWD_LAZY) tile_max(nxt);
         }
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             pin(l0[qb]);
             pin(l1[qb]);
-            pin(mt[qb]);
+            if (!FA_FWD_LAZY) pin(mt[qb]);
         }
     };
     // ring step t: tile t+1 (keys of the next scores) has landed and is visible
@@ -416,6 +464,10 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
             scores(0, sacc);
             if (nfull == 0) mask(0, sacc);
             tile_max(sacc);
+            if (FA_FWD_LAZY)  // the reference starts at tile 0's row maximum (finite:
+                              // every row sees key 0)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) raise(qb);
         }
     }
     const std::integral_constant<bool, false> plain;
