@@ -647,6 +647,14 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 #define FA_BWD_GR_DKDV64 4
 #define FA_BWD_GR_DQ64 2
 #endif
+// d = 128, dQ pass: eight waves (one or two barriers per tile, 32- or 64-key
+// tiles) measured 4-5 % slower per backward than four waves with 32-key
+// tiles at 16 heads x 4096 and 2 x 16 heads x 2048 causal; 64-key tiles on
+// four waves were equal.
+#ifndef FA_BWD_W_DQ128  // waves per workgroup and keys per tile of the dQ pass, d = 128
+#define FA_BWD_W_DQ128 4
+#define FA_BWD_DQ_BC128 32
+#endif
 #ifndef FA_BWD_GR_DKDV128  // tiles per LDS barrier, d = 128 (one workgroup of four waves per CU)
 #define FA_BWD_GR_DKDV128 1
 #define FA_BWD_GR_DQ128 1
@@ -674,8 +682,8 @@ struct DkdvChoice {
 
 template <int D>
 struct DqChoice {
-    static constexpr int BC = D == 64 ? FA_BWD_DQ_BC64 : 32;
-    static constexpr int W = D == 64 ? FA_BWD_W_DQ64 : 4;
+    static constexpr int BC = D == 64 ? FA_BWD_DQ_BC64 : FA_BWD_DQ_BC128;
+    static constexpr int W = D == 64 ? FA_BWD_W_DQ64 : FA_BWD_W_DQ128;
     static constexpr int GR = D == 64 ? FA_BWD_GR_DQ64 : FA_BWD_GR_DQ128;
     static constexpr int QB = D == 64 ? FA_BWD_DQ_QB64 : 1;
     using Cfg = DqCfg<D, BC, GR, W, QB>;
