@@ -392,8 +392,8 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         for (int qb = 0; qb < QB; ++qb) {
             if constexpr (LAZY) {
                 // Exponents against the current reference.  Every probability
-                // is <= its lane's sums, so sums <= 2^24 keep P, O and l far
-                // from fp32 overflow; otherwise (an infinite or NaN sum
+                // is <= the larger of its lane's two sums, so sums <= 2^24 keep
+                // P, O and l far from fp32 overflow; otherwise (an infinite sum
                 // included) raise the reference to the row maximum of the tile
                 // and exponentiate again.  Rare: it takes a score more than 20
                 // above the reference in base 2.
