@@ -263,3 +263,26 @@ def test_bench_reads_shader_clock(tmp_path):
     rf = {"bound": "mfma", "peak": 2500.0}
     bench.add_clock(rf, run, None)
     assert rf["sclk_mhz"] is None
+
+
+def test_variant_build_rejects_bad_arguments():
+    """build.py --variant takes a plain name and -DFA_... definitions only
+    (checked before anything is compiled); FA_LIBRARY selects the library the
+    package loads, and a missing one fails the import (no fallback)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "fa_build", os.path.join(ROOT, "flashattention_online_softmax_fa_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    with pytest.raises(ValueError):
+        b.build_variant("../x", ["-DFA_FWD_WG64=4"])
+    with pytest.raises(ValueError):
+        b.build_variant("ok", ["-O0"])
+    with pytest.raises(ValueError):
+        b.build_variant("ok", ["-DNDEBUG"])
+    import subprocess
+    import sys as _sys
+    env = dict(os.environ, FA_LIBRARY=os.path.join(ROOT, "no_such_libfa.so"))
+    r = subprocess.run([_sys.executable, "-c", "import flashattention_online_softmax_fa_amd"],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0 and "no_such_libfa.so is not built" in r.stderr
