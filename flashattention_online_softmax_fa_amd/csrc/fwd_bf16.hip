@@ -16,7 +16,7 @@
 // it, which are refilled right away (so GR tiles are in flight while GR are
 // computed on; fewer barriers per key: d = 64 takes GR = 4 with a 16-slot
 // ring, d = 128 GR = 2 with 8 slots, 2.5 % and 4 % faster than one barrier per
-// tile).
+// tile, and 3-7 % faster than GR = 8 (17 slots) and GR = 4 (9 slots)).
 //
 // Software pipeline.  Step t exponentiates the scores of tile t while the
 // matrix cores compute the scores of tile t+1, then accumulates O with tile
@@ -108,8 +108,9 @@ struct Tile {
     static constexpr int LPW = 2 * NB / W;           // 1 KiB loads per wave per tile (K and V)
     static constexpr int RPI = 1024 / ROWB;          // rows per 1 KiB load
     static_assert(LPW >= 1 && LPW * W == 2 * NB, "K and V tiles split evenly over the waves");
-    static_assert(G == 1 || G == 2 || G == 4, "tiles per barrier");
-    static_assert(STAGES >= (G == 1 ? 3 : 2 * G + 1) && STAGES <= 16, "ring depth");
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8, "tiles per barrier");
+    static_assert(STAGES >= (G == 1 ? 3 : 2 * G + 1) && STAGES <= 20, "ring depth");
+    static_assert(STAGES * 2 * TILEB <= 160 * 1024, "ring fits the 160 KiB LDS");
     static_assert(BC % 32 == 0, "32-key blocks");
     static_assert(W == 4 || W == 8, "4 or 8 waves");
 };
