@@ -636,6 +636,9 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 // backward than four waves and a barrier per tile.  (The dQ pass fits eight
 // waves because it walks each key tile one 32-key block at a time.)  Two
 // query blocks per dQ wave halve its LDS reads but measured 20 % slower.
+// Limited to three or four waves per SIMD the dQ pass fits 127-161 registers
+// without spills (four-wave workgroups, 32- or 64-key tiles), but ran 1-3 %
+// slower per backward at 2 x 16 heads x 4096 and 4 x 16 heads x 2048 causal.
 #ifndef FA_BWD_W_DKDV64  // waves per workgroup, d = 64
 #define FA_BWD_W_DKDV64 8
 #define FA_BWD_W_DQ64 8
