@@ -46,9 +46,17 @@ KERNEL_SOURCES = {
 
 
 def source_hash(name: str) -> str:
-    path = os.path.join(ROOT, "flashattention_online_softmax_fa_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source and the device headers it includes, with
+    comments and white space removed: measured traffic stays valid across
+    changes to comments and layout, and lapses with any change to the code."""
+    import re
+    text = ""
+    for f in (name, "fa_device.h", "fa_internal.h"):
+        with open(os.path.join(ROOT, "flashattention_online_softmax_fa_amd", "csrc", f)) as fh:
+            text += fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return hashlib.sha256("".join(text.split()).encode()).hexdigest()[:16]
 
 
 def parse():

@@ -286,3 +286,31 @@ def test_variant_build_rejects_bad_arguments():
     r = subprocess.run([_sys.executable, "-c", "import flashattention_online_softmax_fa_amd"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0 and "no_such_libfa.so is not built" in r.stderr
+
+
+def test_traffic_hash_ignores_comments_only(tmp_path):
+    """The source hash that keeps measured HBM traffic valid is blind to
+    comments and white space and changes with any change to the code,
+    including the shared device headers."""
+    import importlib.util
+    import shutil
+    spec = importlib.util.spec_from_file_location("bench_mod2", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    src = os.path.join(ROOT, "flashattention_online_softmax_fa_amd", "csrc")
+    dst = tmp_path / "flashattention_online_softmax_fa_amd" / "csrc"
+    dst.mkdir(parents=True)
+    for f in ("bwd.hip", "fa_device.h", "fa_internal.h"):
+        shutil.copy(os.path.join(src, f), dst / f)
+    bench.ROOT = str(tmp_path)
+    h0 = bench.source_hash("bwd.hip")
+    p = dst / "bwd.hip"
+    p.write_text(p.read_text() + "\n// a new comment\n/* and a block\n comment */\n\n")
+    assert bench.source_hash("bwd.hip") == h0
+    p.write_text(p.read_text().replace("constexpr int ST = T::ST;", "constexpr int ST = T::ST + 0;", 1))
+    assert bench.source_hash("bwd.hip") != h0
+    p.write_text(p.read_text().replace("constexpr int ST = T::ST + 0;", "constexpr int ST = T::ST;", 1))
+    assert bench.source_hash("bwd.hip") == h0
+    d = dst / "fa_device.h"
+    d.write_text(d.read_text().replace("kLog2e = 1.4426950408889634f", "kLog2e = 1.4426950408889635f"))
+    assert bench.source_hash("bwd.hip") != h0
