@@ -241,8 +241,7 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
                 hi[kb] = (int)(hi64 > BR - 1 ? BR - 1 : (hi64 < -1 ? -1 : hi64));
             }
         }
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
+        auto probs = [&](int qb) {
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int qi = qb * 32 + 8 * r4 + 4 * g;
@@ -259,13 +258,17 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
                         pacc[qb][kb][r] = p * (pacc[qb][kb][r] - dv[e]);
                     }
             }
-        }
+        };
         // ---- dV^T += dO^T P and dK^T += Q^T dS.  B operand (k-step kq of 16
         //      queries) = registers 8h..8h+7 of block kq/2, so k-slot (g, e) is
         //      query 8*(e/4) + 4g + e%4 of the step; the transposed A operand is
-        //      read in the same slot order and serves the KB key blocks.
+        //      read in the same slot order and serves the KB key blocks.  Each
+        //      query block's P and dS are formed right before its two k-steps,
+        //      so that its products overlap the next block's vector work (3.5 %
+        //      faster at d = 128 than forming all of them first; equal at 64).
 #pragma unroll
         for (int kq = 0; kq < BR / 16; ++kq) {
+            if (kq % 2 == 0) probs(kq / 2);
             bf16x8 pb[KB], sb[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
