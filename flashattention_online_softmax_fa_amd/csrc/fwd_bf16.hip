@@ -19,9 +19,10 @@
 // tile, and 3-7 % faster than GR = 8 (17 slots) and GR = 4 (9 slots)).
 //
 // Software pipeline.  Step t exponentiates the scores of tile t while the
-// matrix cores compute the scores of tile t+1, then accumulates O with tile
-// t's values; the scores of consecutive tiles alternate between two register
-// sets.  Leading tiles that need no mask for any of the wave's rows run a
+// matrix cores compute the scores of tile t+1, and accumulates O with tile
+// t's values one query block at a time, right after that block's
+// exponentials; the scores of consecutive tiles alternate between two
+// register sets.  Leading tiles that need no mask for any of the wave's rows run a
 // mask-free loop; the rest (the ragged end of the keys, the causal diagonal,
 // and the idle steps of waves whose rows end earlier) run a generic one.
 // Mask-free steps do not reduce the tile maximum before exponentiating: they
@@ -350,24 +351,13 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
             pf[qb][ks] = __builtin_bit_cast(bf16x8, w);
         }
     };
-    // O^T += V_u^T P^T of tile u (P^T in pf); V^T read transposed in the same
-    // k-slot order and shared by the QB query blocks
-    auto pv = [&](int u, const bf16x8 (&pf)[QB][BC / 16]) {
-        const uint8_t *vbase = smem + (u % S) * 2 * T::TILEB + T::TILEB;
-#pragma unroll
-        for (int ks = 0; ks < BC / 16; ++ks) {
-#pragma unroll
-            for (int b = 0; b < D / 32; ++b) {
-                const uint8_t *p = vbase + ks * 16 * T::ROWB;
-                const u32x2 lo = tr_read(p + voff[b][0]), hi = tr_read(p + voff[b][1]);
-                const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-                const bf16x8 a = __builtin_bit_cast(bf16x8, w);
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    oacc[qb][b] =
-                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][ks], oacc[qb][b], 0, 0, 0);
-            }
-        }
+    // A operand of O^T += V_u^T P^T for k-step ks and rows 32b.. of V_u^T, read
+    // transposed from the row-major V tile in the k-slot order of P^T
+    auto vfrag = [&](int u, int ks, int b) {
+        const uint8_t *p = smem + (u % S) * 2 * T::TILEB + T::TILEB + ks * 16 * T::ROWB;
+        const u32x2 lo = tr_read(p + voff[b][0]), hi = tr_read(p + voff[b][1]);
+        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+        return __builtin_bit_cast(bf16x8, w);
     };
     auto step = [&](int t, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB], auto generic) {
         constexpr bool GEN = decltype(generic)::value;
@@ -388,7 +378,16 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         const bool next = GEN ? t + 1 < nkt_w : true;
         if (!GEN || next) scores((t + 1) % S, nxt);
 
+        // ---- per query block: probabilities, then O^T += V_t^T P^T at once, so
+        //      that one block's products overlap the next block's exponentials
+        //      (1.8 % faster at d = 64 than all products after all blocks).  The
+        //      V^T fragments are read once and serve every block.
         bf16x8 pf[QB][BC / 16];
+        bf16x8 va[BC / 16][D / 32];
+#pragma unroll
+        for (int ks = 0; ks < BC / 16; ++ks)
+#pragma unroll
+            for (int b = 0; b < D / 32; ++b) va[ks][b] = vfrag(t, ks, b);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             if constexpr (LAZY) {
@@ -417,8 +416,13 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
             } else {
                 probs(qb, cur, pf, l0[qb], l1[qb]);
             }
+#pragma unroll
+            for (int ks = 0; ks < BC / 16; ++ks)
+#pragma unroll
+                for (int b = 0; b < D / 32; ++b)
+                    oacc[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks][b], pf[qb][ks],
+                                                                          oacc[qb][b], 0, 0, 0);
         }
-        pv(t, pf);
         if (!GEN || next) {
             if (GEN && t + 1 >= nfull) mask(t + 1, nxt);
             if (!FA_FWD_LAZY) tile_max(nxt);
