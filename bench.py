@@ -18,6 +18,10 @@ over the same interval): under these loads the clock stays below the 2.4 GHz
 the published matrix peak assumes, and ``frac_at_sclk`` is the sustained rate
 over the peak scaled to the clock measured.
 
+--sweep times the bf16 forward (d = 64 and 128, with and without the causal
+mask) and the causal backward over sequence lengths 512 .. 16384 at a fixed
+2^18 tokens per call (B = 1, H = 2^18 / N), one JSON line per shape.
+
 --workload selects another workload as the primary one.  --copy-calibration
 runs a plain device copy of known size (for scaling rocprofv3 FETCH_SIZE and
 WRITE_SIZE counters to bytes).  Only one GPU is used; --gpus N > 1 exits.
@@ -75,6 +79,8 @@ def parse():
     p.add_argument("--clock-s", type=float, default=1.5,
                    help="seconds of extra steps per workload while the clock is sampled (0: off)")
     p.add_argument("--copy-calibration", action="store_true")
+    p.add_argument("--sweep", action="store_true",
+                   help="forward and backward over sequence lengths; one JSON line per shape")
     return p.parse_args()
 
 
@@ -341,6 +347,40 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
 
 
+def sweep(torch, fa, steps, warmup, settle_s):
+    """TFLOP/s of the forward and the causal backward over sequence lengths at
+    a fixed number of tokens (one JSON line per shape)."""
+    from fa_inputs import make_inputs
+    for d in (64, 128):
+        for n in (512, 1024, 2048, 4096, 8192, 16384):
+            h = (1 << 18) // n
+            x = make_inputs(1, h, n, n, d, "bf16", seed=n + d, device="cuda", backward=True)
+            scale = 1.0 / math.sqrt(d)
+            o = torch.empty_like(x.q)
+            lse = torch.empty((1, h, n), dtype=torch.float32, device="cuda")
+            ws = torch.empty(fa.fa_bwd_workspace_size(x.q.dtype, 1, h, n, d), dtype=torch.uint8,
+                             device="cuda")
+            g = [torch.empty_like(x.q) for _ in range(3)]
+            for what, causal in (("fwd", False), ("fwd", True), ("bwd", True)):
+                if what == "fwd":
+                    def step():
+                        fa.fa_fwd(x.q, x.k, x.v, o, lse, scale, causal)
+                    flops = 4.0 * h * n * n * d
+                else:
+                    fa.fa_fwd(x.q, x.k, x.v, o, lse, scale, causal)
+                    def step():
+                        fa.fa_bwd(x.q, x.k, x.v, o, lse, x.do, g[0], g[1], g[2], ws, scale, causal)
+                    flops = 10.0 * h * n * n * d
+                flops *= 0.5 if causal else 1.0
+                ms = timed(torch, step, steps, warmup, settle_s)
+                tf = flops / ms / 1e9
+                print(json.dumps({"pass": what, "B": 1, "H": h, "N": n, "d": d, "causal": causal,
+                                  "ms": round(ms, 5), "TFLOP/s": round(tf, 1),
+                                  "frac": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
+            del x, o, lse, ws, g
+            torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -352,6 +392,9 @@ def main():
     import flashattention_online_softmax_fa_amd as fa
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.sweep:
+        sweep(torch, fa, args.steps, args.warmup, args.settle)
         return
     run = setup(args.workload, fa, torch, args.n_split)
     ms = measure(run, torch, args.steps, args.warmup, args.settle)
