@@ -15,8 +15,10 @@
  *                         maximum was raised and the accumulator rescaled (the
  *                         page counts every increase of the maximum; these
  *                         kernels raise it only when the tile maximum exceeds
- *                         it by more than 2^8, so the count is at most the
- *                         page's and equals it when every increase is larger);
+ *                         it by more than 2^8 (tiles that need a mask) or a
+ *                         lane's sum of the tile's probabilities exceeds 2^24
+ *                         (the rest), so the count is at most the page's and
+ *                         equals it when every increase is larger than 2^28);
  *   FA_STAT_BWD_KV_TILES  (key block, query tile) pairs computed by the
  *                         key-major dK/dV pass;
  *   FA_STAT_BWD_Q_TILES   (query block, key tile) pairs computed by the
