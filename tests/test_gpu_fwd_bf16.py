@@ -123,7 +123,7 @@ def test_full_workload_sampled(fa, name, causal):
     assert float(np.abs(got_l - L_ref).max()) <= L_TOL
 
 
-@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("causal", [False, True, "offset"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_rising_scores(fa, d, causal):
     """Base-2 scores q.k * scale * log2(e) close to +j for key j in the even
@@ -133,18 +133,22 @@ def test_rising_scores(fa, d, causal):
     The running maximum, the rescale of O and l, and the logsumexp (about 200
     in natural units) must all follow."""
     B, H, N = 1, 2, 300
-    x = make_inputs(B, H, N, N, d, "bf16", seed=77 + d + causal, device="cpu")
+    Nq, qs = (200, 90) if causal == "offset" else (N, 0)  # offset: row i at key qs + i
+    x = make_inputs(B, H, Nq, N, d, "bf16", seed=77 + d + (causal is True), device="cpu")
     scale = 1 / math.sqrt(d)
     c = scale / math.log(2)
     q = x.q.float() * 0.1
     k = x.k.float() * 0.1
-    q[..., 0] = torch.where(torch.arange(N) % 2 == 0, 1.0, -1.0)
+    q[..., 0] = torch.where(torch.arange(Nq) % 2 == 0, 1.0, -1.0)
     k[..., 0] = torch.arange(N, dtype=torch.float32) / c
     qb, kb = q.to(torch.bfloat16), k.to(torch.bfloat16)
     say(f"bf16 fwd rising scores d={d} causal={causal}")
-    o, lse = fa.forward(qb.cuda(), kb.cuda(), x.v.cuda(), scale, causal)
+    if causal == "offset":
+        o, lse = fa.forward(qb.cuda(), kb.cuda(), x.v.cuda(), scale, q_start=qs)
+    else:
+        o, lse = fa.forward(qb.cuda(), kb.cuda(), x.v.cuda(), scale, causal)
     torch.cuda.synchronize()
-    O_ref, L_ref = oracle.dense_fwd(host(qb), host(kb), host(x.v), scale, causal)
+    O_ref, L_ref = oracle.dense_fwd(host(qb), host(kb), host(x.v), scale, bool(causal), q_start=qs)
     assert float(np.abs(L_ref).max()) > 150  # the case really has large logits
     assert max_abs(o, O_ref) <= O_TOL
     assert max_abs(lse, L_ref) <= L_TOL
