@@ -152,3 +152,25 @@ def test_rising_scores(fa, d, causal):
     assert float(np.abs(L_ref).max()) > 150  # the case really has large logits
     assert max_abs(o, O_ref) <= O_TOL
     assert max_abs(lse, L_ref) <= L_TOL
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_long_sequence_sampled(fa, d, causal):
+    """One head of 65536 queries and keys: 2048 key tiles per wave, the K/V
+    ring wrapping around 128 (d = 64) or 256 (d = 128) times, and the last
+    rows seeing every key.
+    Sampled rows (the first, the last, and seeded ones) against the oracle."""
+    N = 65536
+    say(f"bf16 fwd long sequence N={N} d={d} causal={causal}")
+    x = make_inputs(1, 1, N, N, d, "bf16", seed=65 + d + causal, device="cuda")
+    scale = 1 / math.sqrt(d)
+    o, lse = _run(fa, x, scale, causal)
+    rng = np.random.default_rng(d + causal)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, N - 33, N - 2, N - 1],
+                                     rng.integers(0, N, 40)])).astype(np.int64)
+    O_ref, L_ref = oracle.dense_fwd(host(x.q), host(x.k), host(x.v), scale, causal, rows=rows)
+    got_o = host(o).reshape(-1, d)[rows]
+    got_l = host(lse).reshape(-1)[rows]
+    assert float(np.abs(got_o - O_ref).max()) <= O_TOL
+    assert float(np.abs(got_l - L_ref).max()) <= L_TOL
