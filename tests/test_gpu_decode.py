@@ -133,3 +133,18 @@ def test_decode_full_size_sampled(fa, decode_full, n_split):
     assert max_abs(flat_l[idx], L_ref) <= 1e-3
     _check_states(pm.reshape(B * H, 1, n_split)[idx], pl.reshape(B * H, 1, n_split)[idx],
                   po.reshape(B * H, 1, n_split, d)[idx], rm, rl, ro)
+
+
+@pytest.mark.parametrize("n_split", [16, 64, 1000])
+def test_decode_long_cache(fa, n_split):
+    """One query row against 2^20 - 5 cached keys (d = 128): long chunks per
+    split, uneven split bounds (floor(Nk*s/n)), and the merge of many states."""
+    Nk = (1 << 20) - 5
+    say(f"decode long cache Nk={Nk} n_split={n_split}")
+    x = make_inputs(1, 2, 1, Nk, 128, "bf16", seed=n_split, device="cuda")
+    scale = 1 / math.sqrt(128)
+    o, lse, _ = fa.decode(x.q, x.k, x.v, n_split, scale)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.dense_fwd(host(x.q), host(x.k), host(x.v), scale)
+    assert max_abs(o, O_ref) <= 2e-2
+    assert max_abs(lse, L_ref) <= 1e-3
