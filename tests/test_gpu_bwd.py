@@ -102,3 +102,21 @@ def test_full_workload(fa):
     for got, key in ((dq, "dQ"), (dk, "dK"), (dv, "dV")):
         sel = got.reshape(B * H, N, d)[idx]
         assert max_rel(sel, g[key][0]) <= REL, key
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_long_sequence_identities(fa, d):
+    """Two heads of 32768 tokens, causal (up to 512 query tiles of 64 per
+    key block at d = 64): gradients finite, and on every head the two identities that hold
+    at any size, sum_j dK_j = 0 (each row of dS sums to zero) and
+    sum_j dV_j = sum_i dO_i (each row of P sums to one)."""
+    N = 32768
+    say(f"bwd long sequence N={N} d={d}")
+    x = make_inputs(1, 2, N, N, d, "bf16", seed=32 + d, device="cuda", backward=True)
+    dq, dk, dv = _fwd_bwd(fa, x, 1 / math.sqrt(d), True)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    sum_dk = dk.float().sum(2)
+    assert (sum_dk.abs() <= 2e-2 * dk.float().abs().sum(2) + 1e-3).all()
+    sum_dv, sum_do = dv.float().sum(2), x.do.float().sum(2)
+    assert ((sum_dv - sum_do).abs().max() / sum_do.abs().max()).item() <= 2e-2
