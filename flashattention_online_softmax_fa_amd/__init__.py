@@ -117,33 +117,75 @@ def _scale(d: int, scale) -> float:
 
 
 def _bhnd(t: torch.Tensor):
-    if t.dim() != 4:
+    if not isinstance(t, torch.Tensor) or t.dim() != 4:
         raise ValueError("expected a [B, H, N, d] tensor")
-    return t.shape
+    return tuple(t.shape)
+
+
+def _operands(where: str, dtype, device, **spec) -> None:
+    """Check every operand against the shape the C call will assume from the
+    sizes it is given, and against one dtype and one device: a mismatch would
+    otherwise make a kernel read or write past the end of a buffer.  `spec`
+    maps a name to (tensor, shape, dtype); dtype None means the common one.
+    Raises ValueError before anything reaches the library."""
+    for name, (t, shape, dt) in spec.items():
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{where}: {name} must be a tensor")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{where}: {name} has shape {tuple(t.shape)}, "
+                             f"expected {tuple(shape)}")
+        want = dtype if dt is None else dt
+        if t.dtype != want:
+            raise ValueError(f"{where}: {name} is {t.dtype}, expected {want}")
+        if t.device != device:
+            raise ValueError(f"{where}: {name} is on {t.device}, expected {device}")
+
+
+def _fwd_operands(where, q, k, v, o, lse):
+    B, H, Nq, d = _bhnd(q)
+    Nk = _bhnd(k)[2]
+    f32 = torch.float32
+    _operands(where, q.dtype, q.device, k=(k, (B, H, Nk, d), None), v=(v, (B, H, Nk, d), None),
+              o=(o, (B, H, Nq, d), None), lse=(lse, (B, H, Nq), f32))
+    return B, H, Nq, Nk, d
+
+
+def _bwd_operands(where, q, k, v, o, lse, do, dq, dk, dv, workspace):
+    B, H, Nq, Nk, d = _fwd_operands(where, q, k, v, o, lse)
+    _operands(where, q.dtype, q.device, do=(do, (B, H, Nq, d), None),
+              dq=(dq, (B, H, Nq, d), None), dk=(dk, (B, H, Nk, d), None),
+              dv=(dv, (B, H, Nk, d), None))
+    if not isinstance(workspace, torch.Tensor) or workspace.device != q.device:
+        raise ValueError(f"{where}: workspace must be a tensor on {q.device}")
+    return B, H, Nq, Nk, d
+
+
+def _decode_operands(where, q, k, v, part_m, part_l, part_o, n_split):
+    B, H, Nq, d = _bhnd(q)
+    Nk = _bhnd(k)[2]
+    n = int(n_split)
+    f32 = torch.float32
+    _operands(where, q.dtype, q.device, k=(k, (B, H, Nk, d), None), v=(v, (B, H, Nk, d), None),
+              part_m=(part_m, (B, H, Nq, n), f32), part_l=(part_l, (B, H, Nq, n), f32),
+              part_o=(part_o, (B, H, Nq, n, d), f32))
+    return B, H, Nq, Nk, d
 
 
 def fa_fwd(q, k, v, o, lse, scale=None, causal=False, stream=None) -> None:
-    B, H, Nq, d = _bhnd(q)
-    Nk = _bhnd(k)[2]
-    if lse.dtype != torch.float32:
-        raise TypeError("lse must be float32")
+    B, H, Nq, Nk, d = _fwd_operands("fa_fwd", q, k, v, o, lse)
     _check(_lib.fa_fwd(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
                        _scale(d, scale), int(bool(causal)), _stream(stream)), "fa_fwd")
 
 
 def fa_fwd_offset(q, k, v, o, lse, q_start, scale=None, stream=None) -> None:
-    B, H, Nq, d = _bhnd(q)
-    Nk = _bhnd(k)[2]
-    if lse.dtype != torch.float32:
-        raise TypeError("lse must be float32")
+    B, H, Nq, Nk, d = _fwd_operands("fa_fwd_offset", q, k, v, o, lse)
     _check(_lib.fa_fwd_offset(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq,
                               Nk, d, _scale(d, scale), int(q_start), _stream(stream)),
            "fa_fwd_offset")
 
 
 def fa_fwd_blocked(q, k, v, o, lse, kv_block, scale=None, causal=False, stream=None) -> None:
-    B, H, Nq, d = _bhnd(q)
-    Nk = _bhnd(k)[2]
+    B, H, Nq, Nk, d = _fwd_operands("fa_fwd_blocked", q, k, v, o, lse)
     _check(_lib.fa_fwd_blocked(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq,
                                Nk, d, _scale(d, scale), int(bool(causal)), int(kv_block),
                                _stream(stream)), "fa_fwd_blocked")
@@ -156,8 +198,7 @@ def fa_bwd_workspace_size(dtype, B, H, Nq, d) -> int:
 
 def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, workspace, scale=None, causal=False,
            stream=None) -> None:
-    B, H, Nq, d = _bhnd(q)
-    Nk = _bhnd(k)[2]
+    B, H, Nq, Nk, d = _bwd_operands("fa_bwd", q, k, v, o, lse, do, dq, dk, dv, workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(_lib.fa_bwd(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
                        _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, Nq, Nk, d,
@@ -166,8 +207,8 @@ def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, workspace, scale=None, causal=False,
 
 def fa_bwd_offset(q, k, v, o, lse, do, dq, dk, dv, workspace, q_start, scale=None,
                   stream=None) -> None:
-    B, H, Nq, d = _bhnd(q)
-    Nk = _bhnd(k)[2]
+    B, H, Nq, Nk, d = _bwd_operands("fa_bwd_offset", q, k, v, o, lse, do, dq, dk, dv,
+                                    workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(_lib.fa_bwd_offset(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, Nq,
@@ -176,8 +217,8 @@ def fa_bwd_offset(q, k, v, o, lse, do, dq, dk, dv, workspace, q_start, scale=Non
 
 
 def fa_decode_split(q, k, v, part_m, part_l, part_o, n_split, scale=None, stream=None) -> None:
-    B, H, Nq, d = _bhnd(q)
-    Nk = _bhnd(k)[2]
+    B, H, Nq, Nk, d = _decode_operands("fa_decode_split", q, k, v, part_m, part_l, part_o,
+                                       n_split)
     _check(_lib.fa_decode_split(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(part_m), _ptr(part_l),
                                 _ptr(part_o), B, H, Nq, Nk, d, int(n_split), _scale(d, scale),
                                 _stream(stream)), "fa_decode_split")
@@ -185,8 +226,8 @@ def fa_decode_split(q, k, v, part_m, part_l, part_o, n_split, scale=None, stream
 
 def fa_decode_split_offset(q, k, v, part_m, part_l, part_o, n_split, q_start, scale=None,
                            stream=None) -> None:
-    B, H, Nq, d = _bhnd(q)
-    Nk = _bhnd(k)[2]
+    B, H, Nq, Nk, d = _decode_operands("fa_decode_split_offset", q, k, v, part_m, part_l,
+                                       part_o, n_split)
     _check(_lib.fa_decode_split_offset(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(part_m),
                                        _ptr(part_l), _ptr(part_o), B, H, Nq, Nk, d, int(n_split),
                                        _scale(d, scale), int(q_start), _stream(stream)),
@@ -194,8 +235,16 @@ def fa_decode_split_offset(q, k, v, part_m, part_l, part_o, n_split, q_start, sc
 
 
 def fa_merge_states(part_m, part_l, part_o, o, lse, stream=None) -> None:
+    if not isinstance(part_m, torch.Tensor) or part_m.dim() != 4:
+        raise ValueError("fa_merge_states: part_m must be a [B, H, Nq, n_split] tensor")
     B, H, Nq, n_split = part_m.shape
-    d = o.shape[-1]
+    d = _bhnd(o)[3]
+    if o.dtype not in _DT:
+        raise ValueError(f"fa_merge_states: o is {o.dtype}, expected float32 or bfloat16")
+    f32 = torch.float32
+    _operands("fa_merge_states", f32, part_m.device, part_l=(part_l, (B, H, Nq, n_split), None),
+              part_o=(part_o, (B, H, Nq, n_split, d), None), o=(o, (B, H, Nq, d), o.dtype),
+              lse=(lse, (B, H, Nq), None))
     _check(_lib.fa_merge_states(_dt(o), _ptr(part_m), _ptr(part_l), _ptr(part_o), _ptr(o),
                                 _ptr(lse), B, H, Nq, d, n_split, _stream(stream)),
            "fa_merge_states")

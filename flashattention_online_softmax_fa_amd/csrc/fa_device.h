@@ -189,8 +189,8 @@ __device__ __forceinline__ void dma4(const void *src, uint8_t *dst) { dma4(src, 
 struct TileId {
     uint32_t head, rank;
 };
-__device__ __forceinline__ TileId tile_order(uint32_t bid, uint32_t heads, uint32_t tiles,
-                                             uint32_t group) {
+__host__ __device__ __forceinline__ TileId tile_order(uint32_t bid, uint32_t heads,
+                                                      uint32_t tiles, uint32_t group) {
     uint32_t x = 0, r = bid, hx = heads;
     if (heads % 8u == 0) {
         x = bid % 8u;
