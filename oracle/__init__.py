@@ -59,6 +59,12 @@ def _lib():
         lib.oracle_dense_bwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64,
                                          _i64, _i64, _i64, _i64, _i64, ctypes.c_double,
                                          ctypes.c_int, _i64, _ip, _i64, ctypes.c_int]
+        lib.oracle_bwd_query_rows.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64,
+                                              _i64, _i64, _i64, _i64, _i64, ctypes.c_double,
+                                              ctypes.c_int, _i64, _ip, _i64, ctypes.c_int]
+        lib.oracle_bwd_key_rows.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64,
+                                            _i64, _i64, _i64, _i64, ctypes.c_double,
+                                            ctypes.c_int, _i64, _ip, _i64, ctypes.c_int]
         lib.oracle_state.argtypes = [_dp, _dp, _i64, _i64, _dp, _dp, _dp]
         lib.oracle_state.restype = None
         lib.oracle_merge.argtypes = [ctypes.c_double, ctypes.c_double, _dp, ctypes.c_double,
@@ -68,7 +74,7 @@ def _lib():
                                             _i64, _i64, _i64, _i64, _i64, ctypes.c_double, _ip,
                                             _i64, ctypes.c_int]
         for f in ("oracle_dense_fwd", "oracle_online_fwd", "oracle_dense_bwd",
-                  "oracle_split_decode"):
+                  "oracle_bwd_query_rows", "oracle_bwd_key_rows", "oracle_split_decode"):
             getattr(lib, f).restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -174,23 +180,81 @@ def dense_bwd(Q, K, V, dO, scale: float, causal: bool = False, q_start: int = 0,
     return out
 
 
+def _central_difference(f, theta: np.ndarray, h: float) -> np.ndarray:
+    """Gradient of the scalar function f at the parameter vector theta by
+    central differences, (f(theta + h e_n) - f(theta - h e_n)) / 2h for every
+    coordinate n, with theta restored after each pair of evaluations."""
+    grad = np.empty_like(theta)
+    for n in range(theta.size):
+        x0 = theta[n]
+        theta[n] = x0 + h
+        up = f(theta)
+        theta[n] = x0 - h
+        down = f(theta)
+        theta[n] = x0
+        grad[n] = (up - down) / (2.0 * h)
+    return grad
+
+
 def fd_grad(Q, K, V, dO, scale: float, causal: bool = False, h: float = 1e-5):
-    """Central differences of f = sum(dense_fwd(Q, K, V) * dO) with step h, one
-    element at a time (finite_difference in lab.py).  Tiny inputs only."""
-    Q, K, V, dO = (np.array(x, dtype=np.float64, copy=True) for x in (Q, K, V, dO))
-    grads = []
-    for arr in (Q, K, V):
-        g = np.zeros_like(arr)
-        for idx in np.ndindex(arr.shape):
-            old = arr[idx]
-            arr[idx] = old + h
-            plus = float(np.sum(dense_fwd(Q, K, V, scale, causal, nthreads=1)[0] * dO))
-            arr[idx] = old - h
-            minus = float(np.sum(dense_fwd(Q, K, V, scale, causal, nthreads=1)[0] * dO))
-            arr[idx] = old
-            g[idx] = (plus - minus) / (2.0 * h)
-        grads.append(g)
-    return tuple(grads)
+    """Central-difference gradients (dQ, dK, dV) of f = sum(O * dO), O the
+    dense definition, with step h (the numerical check of lab.py,
+    finite_difference, with the same h).  Q, K and V are packed into one
+    parameter vector.  Tiny inputs only."""
+    arrays = [np.asarray(x, dtype=np.float64) for x in (Q, K, V)]
+    dO = np.asarray(dO, dtype=np.float64)
+    shapes = [a.shape for a in arrays]
+    cuts = np.cumsum([a.size for a in arrays])[:-1]
+    theta = np.concatenate([a.ravel() for a in arrays])
+
+    def f(t):
+        q, k, v = (p.reshape(shp) for p, shp in zip(np.split(t, cuts), shapes))
+        return float(np.sum(dense_fwd(q, k, v, scale, causal, nthreads=1)[0] * dO))
+
+    grad = _central_difference(f, theta, h)
+    return tuple(p.reshape(shp) for p, shp in zip(np.split(grad, cuts), shapes))
+
+
+def bwd_rows(Q, K, V, dO, scale: float, causal: bool = False, q_start: int = 0,
+             query_rows=None, key_rows=None, nthreads: int | None = None):
+    """The backward (dense_bwd's formulas) restricted to chosen rows, for
+    checks where the whole backward is too slow.  ``query_rows`` are flat ids
+    (b*H + h)*Nq + i and give dQ [n, d] (with O, L and D of those rows);
+    ``key_rows`` are flat ids (b*H + h)*Nk + j and give dK [n, d], dV [n, dv],
+    summed over every query that sees the key, with L and D of those queries
+    from this oracle's own forward."""
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    _check4(Q, K, V, dO)
+    B, H, Nq, d = Q.shape
+    Nk, dv = K.shape[2], V.shape[3]
+    nt = nthreads or default_threads()
+    out = {}
+    if query_rows is not None:
+        rows = np.ascontiguousarray(np.asarray(query_rows, dtype=np.int64))
+        out.update(dQ=np.empty((rows.size, d)), O=np.empty((rows.size, dv)),
+                   L=np.empty(rows.size), D=np.empty(rows.size))
+        st = _lib().oracle_bwd_query_rows(_p(Q), _p(K), _p(V), _p(dO), _p(out["dQ"]),
+                                          _p(out["O"]), _p(out["L"]), _p(out["D"]), B, H, Nq,
+                                          Nk, d, dv, float(scale), int(bool(causal)),
+                                          int(q_start), rows.ctypes.data_as(_ip), rows.size, nt)
+        if st != 0:
+            raise ValueError("a query row sees no key")
+    if key_rows is not None:
+        keys = np.ascontiguousarray(np.asarray(key_rows, dtype=np.int64))
+        # L and D of every query of the heads involved (other heads stay NaN)
+        heads = np.unique(keys // Nk)
+        L = np.full(B * H * Nq, np.nan)
+        D = np.full(B * H * Nq, np.nan)
+        qrows = (heads[:, None] * Nq + np.arange(Nq)[None, :]).ravel()
+        O_r, L_r = dense_fwd(Q, K, V, scale, causal, q_start, rows=qrows, nthreads=nt)
+        L[qrows] = L_r
+        D[qrows] = np.sum(dO.reshape(-1, dv)[qrows] * O_r, axis=1)
+        out.update(dK=np.empty((keys.size, d)), dV=np.empty((keys.size, dv)))
+        _lib().oracle_bwd_key_rows(_p(Q), _p(K), _p(V), _p(dO), _p(L), _p(D), _p(out["dK"]),
+                                   _p(out["dV"]), B, H, Nq, Nk, d, dv, float(scale),
+                                   int(bool(causal)), int(q_start), keys.ctypes.data_as(_ip),
+                                   keys.size, nt)
+    return out
 
 
 def state(s, v):

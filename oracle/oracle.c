@@ -26,6 +26,7 @@
  *   oracle_dense_fwd   -- the definition: whole score row, max, exp, sum.
  *   oracle_online_fwd  -- the per-row online softmax over key blocks.
  *   oracle_dense_bwd   -- dQ, dK, dV of <O, dO> by the softmax Jacobian.
+ *   oracle_bwd_query_rows / oracle_bwd_key_rows -- the same for chosen rows.
  *   oracle_state / oracle_merge -- (m, l, o) segment summaries and their merge.
  *   oracle_split_decode -- split the keys, summarise each split, fold merges.
  */
@@ -178,43 +179,45 @@ static void online_row(void *vctx, int64_t item)
     const double *K = a->K + bh * a->Nk * a->d;
     const double *V = a->V + bh * a->Nk * a->dv;
     double *o = a->O + row * a->dv;
+    /* The visible keys are the prefix 0 .. nvis-1; it is cut into blocks of
+     * `block` keys (the last one shorter), visited in order. */
     int64_t nvis = visible_keys(i, a->Nk, a->causal, a->q_start);
-    double *num = (double *)calloc((size_t)a->dv, sizeof(double));
-    double *s = (double *)malloc((size_t)a->block * sizeof(double));
-    double m = -INFINITY, l = 0.0;
-    for (int64_t start = 0; start < a->Nk; start += a->block) {
-        int64_t stop = start + a->block;
-        if (stop > a->Nk) stop = a->Nk;
-        if (stop > nvis) stop = nvis;
-        if (stop <= start) continue; /* the whole block is masked */
-        double bmax = -INFINITY;
-        for (int64_t j = start; j < stop; ++j) {
-            s[j - start] = a->scale * dot(q, K + j * a->d, a->d);
-            bmax = s[j - start] > bmax ? s[j - start] : bmax;
-        }
-        double m_new = m > bmax ? m : bmax;
-        double alpha = (l == 0.0) ? 0.0 : exp(m - m_new);
-#ifdef ORACLE_PLANT_NO_RESCALE
-        alpha = 1.0;
-#endif
-        double bsum = 0.0;
-        for (int64_t c = 0; c < a->dv; ++c) num[c] *= alpha;
-        for (int64_t j = start; j < stop; ++j) {
-            double e = exp(s[j - start] - m_new);
-            bsum += e;
-            for (int64_t c = 0; c < a->dv; ++c) num[c] += e * V[j * a->dv + c];
-        }
-        l = alpha * l + bsum;
-        m = m_new;
-    }
     if (nvis == 0) {
         a->status = 1;
         for (int64_t c = 0; c < a->dv; ++c) o[c] = NAN;
         a->L[row] = NAN;
-    } else {
-        for (int64_t c = 0; c < a->dv; ++c) o[c] = num[c] / l;
-        a->L[row] = m + log(l);
+        return;
     }
+    double *num = (double *)calloc((size_t)a->dv, sizeof(double));
+    double *s = (double *)malloc((size_t)a->block * sizeof(double));
+    /* running state after the blocks seen so far: maximum m, denominator l,
+     * unnormalised numerator num (all three relative to m) */
+    double m = -INFINITY, l = 0.0;
+    for (int64_t j0 = 0; j0 < nvis; j0 += a->block) {
+        int64_t nb = nvis - j0 < a->block ? nvis - j0 : a->block;
+        double bmax = -INFINITY;
+        for (int64_t t = 0; t < nb; ++t) {
+            s[t] = a->scale * dot(q, K + (j0 + t) * a->d, a->d);
+            if (s[t] > bmax) bmax = s[t];
+        }
+        double m_new = bmax > m ? bmax : m;
+        /* old state rebased onto the new maximum; there is none before the
+         * first block, so nothing is carried (and -inf - -inf never formed) */
+        double alpha = j0 == 0 ? 0.0 : exp(m - m_new);
+#ifdef ORACLE_PLANT_NO_RESCALE
+        alpha = 1.0;
+#endif
+        l *= alpha;
+        for (int64_t c = 0; c < a->dv; ++c) num[c] *= alpha;
+        for (int64_t t = 0; t < nb; ++t) {
+            double e = exp(s[t] - m_new);
+            l += e;
+            for (int64_t c = 0; c < a->dv; ++c) num[c] += e * V[(j0 + t) * a->dv + c];
+        }
+        m = m_new;
+    }
+    for (int64_t c = 0; c < a->dv; ++c) o[c] = num[c] / l;
+    a->L[row] = m + log(l);
     free(num);
     free(s);
 }
@@ -332,6 +335,130 @@ int oracle_dense_bwd(const double *Q, const double *K, const double *V, const do
                          scale, causal, q_start, heads, 0};
     parallel_for(heads ? nheads : B * H, nthreads, bwd_head, &a);
     return a.status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* R3 restricted to chosen rows, for checks at sizes where the whole         */
+/* backward is too slow.  The same formulas as bwd_head:                     */
+/*   query row i:  O_i, L_i from the definition, D_i = dO_i . O_i,           */
+/*                 dQ_i = scale sum_j P_ij (dO_i . V_j - D_i) K_j;           */
+/*   key row j:    dV_j = sum_i P_ij dO_i,                                    */
+/*                 dK_j = scale sum_i P_ij (dO_i . V_j - D_i) Q_i,            */
+/*                 over the queries i that see key j, with P_ij =             */
+/*                 exp(S_ij - L_i) and L_i, D_i given by the caller (this     */
+/*                 oracle's own forward of those queries).                    */
+/* flash_backward (attention_kernels.py); backward (lab.py).                 */
+/* ------------------------------------------------------------------------ */
+struct rows_args {
+    const double *Q, *K, *V, *dO, *Lin, *Din;
+    double *out1, *out2, *out3, *out4;
+    int64_t H, Nq, Nk, d, dv;
+    double scale;
+    int causal;
+    int64_t q_start;
+    const int64_t *rows;
+    int status;
+};
+
+static void bwd_query_row(void *vctx, int64_t item)
+{
+    struct rows_args *a = (struct rows_args *)vctx;
+    int64_t row = a->rows[item];
+    int64_t bh = row / a->Nq, i = row % a->Nq;
+    int64_t Nk = a->Nk, d = a->d, dv = a->dv;
+    const double *q = a->Q + row * d;
+    const double *g = a->dO + row * dv;
+    const double *K = a->K + bh * Nk * d;
+    const double *V = a->V + bh * Nk * dv;
+    double *dq = a->out1 + item * d, *o = a->out2 + item * dv;
+    int64_t nvis = visible_keys(i, Nk, a->causal, a->q_start);
+    if (nvis == 0) {
+        a->status = 1;
+        for (int64_t c = 0; c < d; ++c) dq[c] = NAN;
+        for (int64_t c = 0; c < dv; ++c) o[c] = NAN;
+        a->out3[item] = NAN;
+        a->out4[item] = NAN;
+        return;
+    }
+    double *s = (double *)malloc((size_t)nvis * sizeof(double));
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nvis; ++j) {
+        s[j] = a->scale * dot(q, K + j * d, d);
+        if (s[j] > m) m = s[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < nvis; ++j) l += exp(s[j] - m);
+    double lse = m + log(l);
+    for (int64_t c = 0; c < dv; ++c) o[c] = 0.0;
+    for (int64_t j = 0; j < nvis; ++j) {
+        double p = exp(s[j] - lse);
+        for (int64_t c = 0; c < dv; ++c) o[c] += p * V[j * dv + c];
+    }
+    double D = dot(g, o, dv);
+    for (int64_t c = 0; c < d; ++c) dq[c] = 0.0;
+    for (int64_t j = 0; j < nvis; ++j) {
+        double p = exp(s[j] - lse);
+        double ds = p * (dot(g, V + j * dv, dv) - D);
+        for (int64_t c = 0; c < d; ++c) dq[c] += a->scale * ds * K[j * d + c];
+    }
+    a->out3[item] = lse;
+    a->out4[item] = D;
+    free(s);
+}
+
+static void bwd_key_row(void *vctx, int64_t item)
+{
+    struct rows_args *a = (struct rows_args *)vctx;
+    int64_t key = a->rows[item];
+    int64_t bh = key / a->Nk, j = key % a->Nk;
+    int64_t Nq = a->Nq, d = a->d, dv = a->dv;
+    const double *k = a->K + key * d;
+    const double *v = a->V + key * dv;
+    const double *Q = a->Q + bh * Nq * d;
+    const double *dO = a->dO + bh * Nq * dv;
+    const double *L = a->Lin + bh * Nq, *Dv = a->Din + bh * Nq;
+    double *dk = a->out1 + item * d, *dvr = a->out2 + item * dv;
+    for (int64_t c = 0; c < d; ++c) dk[c] = 0.0;
+    for (int64_t c = 0; c < dv; ++c) dvr[c] = 0.0;
+    for (int64_t i = 0; i < Nq; ++i) {
+        if (j >= visible_keys(i, a->Nk, a->causal, a->q_start)) continue;
+        const double *g = dO + i * dv;
+        double p = exp(a->scale * dot(Q + i * d, k, d) - L[i]);
+        double ds = p * (dot(g, v, dv) - Dv[i]);
+        for (int64_t c = 0; c < d; ++c) dk[c] += a->scale * ds * Q[i * d + c];
+        for (int64_t c = 0; c < dv; ++c) dvr[c] += p * g[c];
+    }
+}
+
+/* dQ, O, L, D of the listed query rows (flat ids bh * Nq + i), packed in list
+ * order: dQ [n][d], O [n][dv], L [n], D [n].  Returns 1 if a row sees no key. */
+int oracle_bwd_query_rows(const double *Q, const double *K, const double *V, const double *dO,
+                          double *dQ, double *O, double *L, double *Dv, int64_t B, int64_t H,
+                          int64_t Nq, int64_t Nk, int64_t d, int64_t dv, double scale,
+                          int causal, int64_t q_start, const int64_t *rows, int64_t nrows,
+                          int nthreads)
+{
+    (void)B;
+    struct rows_args a = {Q, K, V, dO, NULL, NULL, dQ, O, L, Dv, H, Nq, Nk, d, dv,
+                          scale, causal, q_start, rows, 0};
+    parallel_for(nrows, nthreads, bwd_query_row, &a);
+    return a.status;
+}
+
+/* dK [n][d] and dV [n][dv] of the listed key rows (flat ids bh * Nk + j),
+ * packed in list order, from the caller's L and D ([B*H*Nq] each: this
+ * oracle's forward of every query of the heads involved). */
+int oracle_bwd_key_rows(const double *Q, const double *K, const double *V, const double *dO,
+                        const double *L, const double *Dv, double *dK, double *dV, int64_t B,
+                        int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv, double scale,
+                        int causal, int64_t q_start, const int64_t *keys, int64_t nkeys,
+                        int nthreads)
+{
+    (void)B;
+    struct rows_args a = {Q, K, V, dO, L, Dv, dK, dV, NULL, NULL, H, Nq, Nk, d, dv,
+                          scale, causal, q_start, keys, 0};
+    parallel_for(nkeys, nthreads, bwd_key_row, &a);
+    return 0;
 }
 
 /* ------------------------------------------------------------------------ */
