@@ -1,9 +1,9 @@
 """MI355X (gfx950) FlashAttention: a thin Python binding over libfa.so.
 
 The functions named like the C entry points (``fa_fwd``, ``fa_fwd_offset``,
-``fa_fwd_blocked``, ``fa_bwd``, ``fa_bwd_offset``, ``fa_bwd_workspace_size``,
-``fa_decode_split``, ``fa_decode_split_offset``, ``fa_merge_states``,
-``fa_status_str``) only check and marshal torch tensors
+``fa_fwd_blocked``, ``fa_bwd``, ``fa_bwd_offset``, ``fa_bwd_noalloc``,
+``fa_bwd_workspace_size``, ``fa_decode_split``, ``fa_decode_split_offset``,
+``fa_merge_states``, ``fa_status_str``) only check and marshal torch tensors
 into the C ABI of ``include/fa.h``; every step of the computation runs in the
 library's HIP kernels.  ``forward``, ``backward`` and ``decode`` additionally
 allocate the outputs with torch before calling them.
@@ -49,6 +49,8 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
                            ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64, _f32, _int, _vp]
     lib.fa_bwd_offset.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64, _f32, _i64, _vp]
+    lib.fa_bwd_noalloc.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                                   _i64, _i64, _i64, _i64, _f32, _int, _vp]
     lib.fa_decode_split.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                     _i64, _i64, _f32, _vp]
     lib.fa_decode_split_offset.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
@@ -58,7 +60,8 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.fa_status_str.argtypes = [_int]
     lib.fa_status_str.restype = ctypes.c_char_p
     for f in ("fa_fwd", "fa_fwd_offset", "fa_fwd_blocked", "fa_bwd", "fa_bwd_offset",
-              "fa_decode_split", "fa_decode_split_offset", "fa_merge_states"):
+              "fa_bwd_noalloc", "fa_decode_split", "fa_decode_split_offset",
+              "fa_merge_states"):
         getattr(lib, f).restype = _int
     return lib
 
@@ -66,8 +69,11 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
 _lib = _declare(ctypes.CDLL(LIB_PATH))
 
 EXPORTS = ("fa_fwd", "fa_fwd_offset", "fa_fwd_blocked", "fa_bwd_workspace_size", "fa_bwd",
-           "fa_bwd_offset", "fa_decode_split", "fa_decode_split_offset", "fa_merge_states",
-           "fa_status_str")
+           "fa_bwd_offset", "fa_bwd_noalloc", "fa_decode_split", "fa_decode_split_offset",
+           "fa_merge_states", "fa_status_str")
+
+# Size of the device array fa_bwd_noalloc keeps its workspace in (include/fa.h).
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class FaError(RuntimeError):
@@ -214,6 +220,25 @@ def fa_bwd_offset(q, k, v, o, lse, do, dq, dk, dv, workspace, q_start, scale=Non
                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, Nq,
                               Nk, d, _scale(d, scale), int(q_start), _stream(stream)),
            "fa_bwd_offset")
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, scale=None, causal=False,
+                   stream=None) -> None:
+    """fa_bwd without a workspace: the library keeps it in a fixed device array
+    of FA_NOALLOC_SCRATCH_BYTES, shared by every call on the GPU (calls that
+    overlap on one GPU race)."""
+    B, H, Nq, Nk, d = _fwd_operands("fa_bwd_noalloc", q, k, v, o, lse)
+    _operands("fa_bwd_noalloc", q.dtype, q.device, do=(do, (B, H, Nq, d), None),
+              dq=(dq, (B, H, Nq, d), None), dk=(dk, (B, H, Nk, d), None),
+              dv=(dv, (B, H, Nk, d), None))
+    need = fa_bwd_workspace_size(q.dtype, B, H, Nq, d) if q.dtype in _DT else 0
+    if need > FA_NOALLOC_SCRATCH_BYTES:
+        raise ValueError(f"fa_bwd_noalloc: {B}*{H}*{Nq} query rows need {need} bytes of "
+                         f"workspace, more than its fixed {FA_NOALLOC_SCRATCH_BYTES} "
+                         "(use fa_bwd with a workspace)")
+    _check(_lib.fa_bwd_noalloc(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                               _ptr(dq), _ptr(dk), _ptr(dv), B, H, Nq, Nk, d, _scale(d, scale),
+                               int(bool(causal)), _stream(stream)), "fa_bwd_noalloc")
 
 
 def fa_decode_split(q, k, v, part_m, part_l, part_o, n_split, scale=None, stream=None) -> None:

@@ -2,6 +2,7 @@
 // per call.  Nothing is enqueued unless every check passes.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/fa.h"
 #include "../../include/fa_stats.h"
@@ -63,6 +64,11 @@ fa_status bwd_common(fa_dtype dt, const void *Q, const void *K, const void *V, c
                      void *workspace, size_t ws_bytes, int64_t B, int64_t H, int64_t Nq,
                      int64_t Nk, int64_t d, float scale, int causal, int64_t q_start,
                      void *stream);
+
+fa_status bwd_noalloc_common(fa_dtype dt, const void *Q, const void *K, const void *V,
+                             const void *O, const float *L, const void *dO, void *dQ, void *dK,
+                             void *dV, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                             float scale, int causal, void *stream);
 
 fa_status decode_common(fa_dtype dt, const void *Q, const void *K, const void *V, float *part_m,
                         float *part_l, float *part_o, int64_t B, int64_t H, int64_t Nq,
@@ -135,15 +141,24 @@ fa_status fa_bwd_offset(fa_dtype dt, const void *Q, const void *K, const void *V
                       scale, 1, q_start, stream);
 }
 
+fa_status fa_bwd_noalloc(fa_dtype dt, const void *Q, const void *K, const void *V, const void *O,
+                         const float *L, const void *dO, void *dQ, void *dK, void *dV, int64_t B,
+                         int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+                         void *stream) {
+    return bwd_noalloc_common(dt, Q, K, V, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal,
+                              stream);
+}
+
 }  // extern "C"
 
 namespace {
 
-fa_status bwd_common(fa_dtype dt, const void *Q, const void *K, const void *V, const void *O,
-                     const float *L, const void *dO, void *dQ, void *dK, void *dV,
-                     void *workspace, size_t ws_bytes, int64_t B, int64_t H, int64_t Nq,
-                     int64_t Nk, int64_t d, float scale, int causal, int64_t q_start,
-                     void *stream) {
+// Every check of a backward call that does not involve the workspace; no HIP
+// call is made.
+fa_status bwd_check(fa_dtype dt, const void *Q, const void *K, const void *V, const void *O,
+                    const float *L, const void *dO, void *dQ, void *dK, void *dV, int64_t B,
+                    int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+                    int64_t q_start) {
     if (!dtype_ok(dt)) return FA_ERR_INVALID_ARG;
     if (!sizes_ok(B, H, Nq, Nk, d)) return FA_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
@@ -152,23 +167,94 @@ fa_status bwd_common(fa_dtype dt, const void *Q, const void *K, const void *V, c
     const uintptr_t al = dt == FA_BF16 ? 16 : 4;
     if (!aligned(Q, al) || !aligned(K, al) || !aligned(V, al) || !aligned(O, al) ||
         !aligned(dO, al) || !aligned(dQ, al) || !aligned(dK, al) || !aligned(dV, al) ||
-        !aligned(L, 4) || !aligned(workspace, 256))
+        !aligned(L, 4))
         return FA_ERR_INVALID_ARG;
-    const size_t need = fa_bwd_workspace_size(dt, B, H, Nq, d);
-    if (ws_bytes < need) return FA_ERR_INVALID_ARG;
-    const size_t half = need / 2;
-    fa::BwdArgs a{Q,  K,  V,  O,  dO, L,  dQ, dK, dV, (float *)workspace,
-                  (float *)((char *)workspace + half), B, H, Nq, Nk, d, scale, causal, q_start};
     if (dt == FA_F32) {
         if (d > 128) return FA_ERR_UNSUPPORTED;
         if ((B * H * Nq + 3) / 4 > kMaxGrid || (B * H * Nk + 3) / 4 > kMaxGrid)
             return FA_ERR_UNSUPPORTED;
-        return hip_status(fa::launch_bwd_f32(a, (hipStream_t)stream));
+        return FA_OK;
     }
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (B * H * ((Nk + 63) / 64) > kMaxGrid || B * H * ((Nq + 63) / 64) > kMaxGrid)
         return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+// Checked arguments and a workspace of fa_bwd_workspace_size() bytes at
+// `workspace`: enqueue the backward.
+fa_status bwd_launch(fa_dtype dt, const void *Q, const void *K, const void *V, const void *O,
+                     const float *L, const void *dO, void *dQ, void *dK, void *dV,
+                     void *workspace, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                     float scale, int causal, int64_t q_start, void *stream) {
+    const size_t half = fa_bwd_workspace_size(dt, B, H, Nq, d) / 2;
+    fa::BwdArgs a{Q,  K,  V,  O,  dO, L,  dQ, dK, dV, (float *)workspace,
+                  (float *)((char *)workspace + half), B, H, Nq, Nk, d, scale, causal, q_start};
+    if (dt == FA_F32) return hip_status(fa::launch_bwd_f32(a, (hipStream_t)stream));
     return hip_status(fa::launch_bwd_bf16(a, (hipStream_t)stream));
+}
+
+fa_status bwd_common(fa_dtype dt, const void *Q, const void *K, const void *V, const void *O,
+                     const float *L, const void *dO, void *dQ, void *dK, void *dV,
+                     void *workspace, size_t ws_bytes, int64_t B, int64_t H, int64_t Nq,
+                     int64_t Nk, int64_t d, float scale, int causal, int64_t q_start,
+                     void *stream) {
+    const fa_status st = bwd_check(dt, Q, K, V, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale,
+                                   causal, q_start);
+    if (st != FA_OK) return st;
+    if (!aligned(workspace, 256)) return FA_ERR_INVALID_ARG;
+    if (ws_bytes < fa_bwd_workspace_size(dt, B, H, Nq, d)) return FA_ERR_INVALID_ARG;
+    return bwd_launch(dt, Q, K, V, O, L, dO, dQ, dK, dV, workspace, B, H, Nq, Nk, d, scale,
+                      causal, q_start, stream);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// The backward's workspace (D and L * log2(e), 8 bytes per query row) in a
+// fixed array of device memory, for fa_bwd_noalloc.  Each GPU the library runs
+// on holds its own copy until the process ends.  In host code `scratch` only
+// names the variable: its device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and kept in g_scratch; only
+// that address is ever passed to a kernel.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
+
+fa_status scratch_of_current_device(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return FA_ERR_HIP;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return FA_OK;
+}
+
+fa_status bwd_noalloc_common(fa_dtype dt, const void *Q, const void *K, const void *V,
+                             const void *O, const float *L, const void *dO, void *dQ, void *dK,
+                             void *dV, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                             float scale, int causal, void *stream) {
+    fa_status st = bwd_check(dt, Q, K, V, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal,
+                             0);
+    if (st != FA_OK) return st;
+    if (fa_bwd_workspace_size(dt, B, H, Nq, d) > (size_t)FA_NOALLOC_SCRATCH_BYTES)
+        return FA_ERR_INVALID_ARG;
+    void *ws = nullptr;
+    st = scratch_of_current_device(&ws);
+    if (st != FA_OK) return st;
+    return bwd_launch(dt, Q, K, V, O, L, dO, dQ, dK, dV, ws, B, H, Nq, Nk, d, scale, causal, 0,
+                      stream);
 }
 
 }  // namespace

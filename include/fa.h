@@ -25,7 +25,9 @@
  *             thread).  bf16 buffers must be 16-byte aligned, fp32 buffers
  *             4-byte aligned.  Inputs and outputs must not overlap.
  * Ownership.  The caller allocates and frees every buffer, workspaces
- *             included.  The library never allocates, frees or synchronises.
+ *             included.  The library never allocates, frees or synchronises
+ *             (fa_bwd_noalloc uses a fixed array inside the library instead
+ *             of a workspace; see there).
  * Streams.    `stream` is a hipStream_t (NULL = the default stream).  Every
  *             call only enqueues work on it and returns; results are ready
  *             when the stream reaches that point.
@@ -33,7 +35,8 @@
  *             call returns FA_ERR_INVALID_ARG or FA_ERR_UNSUPPORTED and
  *             launches nothing.  A failed launch returns FA_ERR_HIP.  Faults
  *             inside kernels surface at the caller's next synchronisation.
- *             No call keeps state between calls; calls are thread-safe.
+ *             No call keeps state between calls; calls are thread-safe
+ *             (except that fa_bwd_noalloc calls on one GPU share its array).
  * Precision.  FA_BF16 inputs are multiplied on bf16 matrix cores with fp32
  *             accumulation; softmax statistics, L, D and partial states are
  *             fp32; bf16 outputs are rounded to nearest even.  FA_F32 runs
@@ -148,6 +151,28 @@ fa_status fa_bwd_offset(fa_dtype dt, const void *Q, const void *K, const void *V
                         const float *L, const void *dO, void *dQ, void *dK, void *dV,
                         void *workspace, size_t ws_bytes, int64_t B, int64_t H, int64_t Nq,
                         int64_t Nk, int64_t d, float scale, int64_t q_start, void *stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument and no allocation of any kind.  The
+ * backward's workspace (D and L * log2(e)) lives instead in a fixed array of
+ * FA_NOALLOC_SCRATCH_BYTES bytes of device memory inside the library, one per
+ * GPU, held until the process ends.
+ *   Arguments and results as fa_bwd (causal: 0 or 1, top-left).
+ *   Limit: fa_bwd_workspace_size(dt, B, H, Nq, d) must not exceed
+ *   FA_NOALLOC_SCRATCH_BYTES, i.e. B * H * Nq <= 2^21 query rows; larger
+ *   calls return FA_ERR_INVALID_ARG and launch nothing.
+ *   Every call on one GPU uses that GPU's one array: calls that overlap on a
+ *   GPU (other streams or threads, before the previous call has finished)
+ *   race and give wrong results.  Calls in order on one stream are safe; the
+ *   array needs no clearing (every value read is written first in the call).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+fa_status fa_bwd_noalloc(fa_dtype dt, const void *Q, const void *K, const void *V,
+                         const void *O, const float *L, const void *dO, void *dQ, void *dK,
+                         void *dV, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                         float scale, int causal, void *stream);
 
 /*
  * fa_decode_split -- first pass of split-KV decoding (Flash-Decoding).

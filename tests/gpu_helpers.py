@@ -14,6 +14,9 @@ def say(*a):
 
 
 def host(t):
+    """fp64 numpy copy of a tensor (or an array already on the host)."""
+    if isinstance(t, np.ndarray):
+        return t.astype(np.float64, copy=False)
     return to_f64_numpy(t)
 
 
@@ -44,3 +47,11 @@ def sample_heads(B, H, k, seed):
     while len(picks) < min(k, n):
         picks.add(int(rng.integers(0, n)))
     return sorted(picks)
+
+
+def head_block(t: torch.Tensor, lo: int, hi: int):
+    """Host fp64 copy [1, hi-lo, N, d] of flat heads lo .. hi-1 (b*H + h) of a
+    [B, H, N, d] tensor; the exact upcast runs on the device, then one copy."""
+    B, H = t.shape[0], t.shape[1]
+    flat = t.reshape((B * H,) + tuple(t.shape[2:]))[lo:hi]
+    return flat.to(torch.float64).cpu().numpy()[None]

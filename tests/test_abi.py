@@ -37,6 +37,8 @@ def lib():
                            i64, i64, i64, f32, i, vp]
     lib.fa_bwd_offset.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64,
                                   i64, i64, i64, i64, f32, i64, vp]
+    lib.fa_bwd_noalloc.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                   i64, f32, i, vp]
     lib.fa_decode_split.argtypes = [i, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32,
                                     vp]
     lib.fa_decode_split_offset.argtypes = [i, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
@@ -50,8 +52,8 @@ def lib():
 def test_header_declares_the_calls():
     assert _declared() == sorted(["fa_fwd", "fa_fwd_offset", "fa_fwd_blocked",
                                   "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_offset",
-                                  "fa_decode_split", "fa_decode_split_offset", "fa_merge_states",
-                                  "fa_status_str"])
+                                  "fa_bwd_noalloc", "fa_decode_split", "fa_decode_split_offset",
+                                  "fa_merge_states", "fa_status_str"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -155,6 +157,39 @@ def bwd(lib, **kw):
 ])
 def test_bwd_rejects(lib, kw, want):
     assert bwd(lib, **kw) == want
+
+
+def bwd_noalloc(lib, **kw):
+    a = dict(dt=FA_BF16, d=64, B=1, H=1, Nq=8, scale=0.125, causal=1, dO=P, dQ=P)
+    a.update(kw)
+    return lib.fa_bwd_noalloc(a["dt"], P, P, P, P, P, a["dO"], a["dQ"], P, P, a["B"], a["H"],
+                              a["Nq"], 8, a["d"], a["scale"], a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dO=NULL), FA_ERR_INVALID_ARG),
+    (dict(dQ=P + 2), FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), FA_ERR_INVALID_ARG),
+    (dict(causal=2), FA_ERR_INVALID_ARG),
+    (dict(Nq=0), FA_ERR_INVALID_ARG),
+    (dict(d=32), FA_ERR_UNSUPPORTED),
+    # beyond the fixed array: 2^21 query rows fit, one more does not
+    (dict(B=2, H=1 << 10, Nq=(1 << 10) + 1), FA_ERR_INVALID_ARG),
+    (dict(B=1, H=1, Nq=(1 << 21) + 1), FA_ERR_INVALID_ARG),
+])
+def test_bwd_noalloc_rejects(lib, kw, want):
+    """Rejected before any HIP call (there is no GPU here): bad arguments as
+    for fa_bwd, and sizes whose workspace would not fit the fixed array."""
+    assert bwd_noalloc(lib, **kw) == want
+
+
+def test_bwd_noalloc_limit_matches_binding():
+    import flashattention_online_softmax_fa_amd as fa
+    text = open(HEADER).read()
+    assert "#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)" in text
+    assert fa.FA_NOALLOC_SCRATCH_BYTES == 16 << 20
+    # 2^21 rows need exactly the whole array
+    assert fa.fa_bwd_workspace_size(FA_BF16, 1, 1, 1 << 21, 64) == fa.FA_NOALLOC_SCRATCH_BYTES
 
 
 def test_decode_rejects(lib):

@@ -4,7 +4,7 @@ O max-abs 2e-2 and L max-abs 1e-3 against the dense definition; per-split
 states against the oracle's split summaries (m max-abs 1e-3; l and o rebased
 to the oracle's m, max-rel 1e-2); the merge on random states against the
 oracle's left fold.  Full-size decode (64 x 32 heads, 32768 keys, d = 128) is
-checked on sampled heads at every split count the benchmark uses."""
+checked on every head at every split count the benchmark uses."""
 import math
 
 import numpy as np
@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from fa_inputs import make_inputs, workload_inputs, WORKLOADS
-from tests.gpu_helpers import heads_slice, host, max_abs, max_rel, sample_heads, say
+from tests.gpu_helpers import head_block, host, max_abs, max_rel, say
 
 pytestmark = pytest.mark.gpu
 
@@ -105,34 +105,51 @@ def test_merge_random_states(fa):
 
 
 @pytest.fixture(scope="module")
-def decode_full():
+def decode_full(fa):
+    """The decode workload (64 x 32 heads, one query, 32768 keys, d = 128) at
+    every split count the benchmark uses: the GPU's O, L and split states on
+    the host, and the oracle's, computed one batch index (32 heads, 0.5 GiB of
+    bf16 K and V) at a time so that host memory stays bounded."""
     say("decode full: generating 64 x 32 x 32768 x 128 bf16 K/V")
     x = workload_inputs("decode_d128", device="cuda")
-    torch.cuda.synchronize()
-    yield x
+    B, H, _, d = x.q.shape
+    scale = 1 / math.sqrt(d)
+    splits = list(WORKLOADS["decode_d128"]["n_split"])
+    got, ref = {}, {n: {"O": [], "L": [], "m": [], "l": [], "o": []} for n in splits}
+    for n in splits:
+        say(f"decode full: GPU at n_split={n}")
+        o, lse, (pm, pl, po) = fa.decode(x.q, x.k, x.v, n, scale)
+        torch.cuda.synchronize()
+        got[n] = tuple(host(t) for t in (o, lse, pm, pl, po))
+        del o, lse, pm, pl, po
+    for b in range(B):
+        if b % 8 == 0:
+            say(f"decode full: oracle on batch index {b}..{b + 7}")
+        Q, K, V = (head_block(t, b * H, (b + 1) * H) for t in (x.q, x.k, x.v))
+        for n in splits:
+            O_r, L_r, rm, rl, ro = oracle.split_decode(Q, K, V, n, scale)
+            for key, val in zip(("O", "L", "m", "l", "o"), (O_r, L_r, rm, rl, ro)):
+                ref[n][key].append(val)
+        del Q, K, V
     del x
     torch.cuda.empty_cache()
+    return got, {n: {k: np.concatenate(v) for k, v in r.items()} for n, r in ref.items()}
 
 
 @pytest.mark.parametrize("n_split", list(WORKLOADS["decode_d128"]["n_split"]))
-def test_decode_full_size_sampled(fa, decode_full, n_split):
-    x = decode_full
-    B, H, _, d = x.q.shape
-    scale = 1 / math.sqrt(d)
-    say(f"decode full n_split={n_split}")
-    o, lse, (pm, pl, po) = fa.decode(x.q, x.k, x.v, n_split, scale)
-    torch.cuda.synchronize()
-    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
-    heads = sample_heads(B, H, 6, seed=n_split)
-    Q, K, V = (heads_slice(t, heads) for t in (x.q, x.k, x.v))
-    O_ref, L_ref, rm, rl, ro = oracle.split_decode(Q, K, V, n_split, scale)
-    flat_o = o.reshape(B * H, 1, d)
-    flat_l = lse.reshape(B * H, 1)
-    idx = torch.tensor(heads, device="cuda")
-    assert max_abs(flat_o[idx], O_ref) <= 2e-2
-    assert max_abs(flat_l[idx], L_ref) <= 1e-3
-    _check_states(pm.reshape(B * H, 1, n_split)[idx], pl.reshape(B * H, 1, n_split)[idx],
-                  po.reshape(B * H, 1, n_split, d)[idx], rm, rl, ro)
+def test_decode_full_size(decode_full, n_split):
+    """Every head of the decode workload: O and L against the split-and-merge
+    oracle (equal to the definition), and every split state."""
+    got, ref = decode_full
+    o, lse, pm, pl, po = got[n_split]
+    r = ref[n_split]
+    BH = r["O"].shape[0]
+    d = r["O"].shape[-1]
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    assert max_abs(o.reshape(BH, 1, d), r["O"]) <= 2e-2
+    assert max_abs(lse.reshape(BH, 1), r["L"]) <= 1e-3
+    _check_states(pm.reshape(BH, 1, n_split), pl.reshape(BH, 1, n_split),
+                  po.reshape(BH, 1, n_split, d), r["m"], r["l"], r["o"])
 
 
 @pytest.mark.parametrize("n_split", [16, 64, 1000])

@@ -5,7 +5,8 @@ oracle; the GPU rounds P to bf16 before the PV product and O on output).
 Mid sizes are compared on every element and span several 128-query and
 64-key tiles with ragged tails; the full workloads (4 x 16 heads x 2048, d=64;
 32 heads x 8192 causal, d=128, with one K row per head scaled by 30) are
-compared on sampled rows, in the launch configuration the benchmark times."""
+compared on every element too, in the launch configuration the benchmark
+times."""
 import math
 
 import numpy as np
@@ -14,7 +15,7 @@ import torch
 
 import oracle
 from fa_inputs import make_inputs, workload_inputs
-from tests.gpu_helpers import host, max_abs, say
+from tests.gpu_helpers import head_block, host, max_abs, say
 
 pytestmark = pytest.mark.gpu
 O_TOL, L_TOL = 2e-2, 1e-3
@@ -92,35 +93,39 @@ def test_uniform_scores_bf16(fa):
     np.testing.assert_allclose(host(lse)[0, 0], np.log(np.arange(1, N + 1)), atol=L_TOL)
 
 
-def _sample_rows(B, H, Nq, n, seed, extra=()):
-    rng = np.random.default_rng(seed)
-    rows = set(int(r) for r in rng.integers(0, B * H * Nq, n))
-    for bh in (0, B * H - 1):
-        for i in (0, 1, 63, 64, 127, 128, Nq - 1) + tuple(extra):
-            if 0 <= i < Nq:
-                rows.add(bh * Nq + i)
-    return np.array(sorted(rows), dtype=np.int64)
-
-
-@pytest.mark.parametrize("name,causal", [("prefill_d64", False), ("prefill_causal_d128", True)])
-def test_full_workload_sampled(fa, name, causal):
-    say(f"bf16 fwd full workload {name}: generating")
-    x = workload_inputs(name, device="cuda")
+def test_full_workload_prefill_d64(fa):
+    """The non-causal d = 64 workload (4 x 16 heads x 2048, 256 workgroups of
+    512 queries dealt to the XCDs by head range), every element of O and L."""
+    say("bf16 fwd full workload prefill_d64: generating")
+    x = workload_inputs("prefill_d64", device="cuda")
     B, H, Nq, d = x.q.shape
     scale = 1 / math.sqrt(d)
-    say(f"bf16 fwd full workload {name}: running")
-    o, lse = _run(fa, x, scale, causal)
+    say("bf16 fwd full workload prefill_d64: running")
+    o, lse = _run(fa, x, scale, False)
+    say("bf16 fwd full workload prefill_d64: oracle on every row")
+    O_ref, L_ref = oracle.dense_fwd(host(x.q), host(x.k), host(x.v), scale, False)
+    assert max_abs(o, O_ref) <= O_TOL
+    assert max_abs(lse, L_ref) <= L_TOL
+
+
+def test_full_workload_prefill_causal_d128(fa):
+    """The causal d = 128 workload with one K row per head scaled by 30
+    (32 heads x 8192, 1024 workgroups of 256 queries), every element of O and
+    L, the oracle run over eight heads at a time."""
+    say("bf16 fwd full workload prefill_causal_d128: generating")
+    x = workload_inputs("prefill_causal_d128", device="cuda")
+    B, H, Nq, d = x.q.shape
+    scale = 1 / math.sqrt(d)
+    say("bf16 fwd full workload prefill_causal_d128: running")
+    o, lse = _run(fa, x, scale, True)
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
-    extra = ()
-    if x.hot_rows is not None:  # rows right at and after a hot key
-        j = int(x.hot_rows[0, 0])
-        extra = (j, j + 1, min(j + 200, Nq - 1))
-    rows = _sample_rows(B, H, Nq, 400, seed=len(name), extra=extra)
-    O_ref, L_ref = oracle.dense_fwd(host(x.q), host(x.k), host(x.v), scale, causal, rows=rows)
-    got_o = host(o).reshape(-1, d)[rows]
-    got_l = host(lse).reshape(-1)[rows]
-    assert float(np.abs(got_o - O_ref).max()) <= O_TOL
-    assert float(np.abs(got_l - L_ref).max()) <= L_TOL
+    for lo in range(0, B * H, 8):
+        say(f"bf16 fwd full workload prefill_causal_d128: oracle on heads {lo}..{lo + 7}")
+        Q, K, V = (head_block(t, lo, lo + 8) for t in (x.q, x.k, x.v))
+        O_ref, L_ref = oracle.dense_fwd(Q, K, V, scale, True)
+        assert max_abs(head_block(o, lo, lo + 8), O_ref) <= O_TOL, f"O, heads {lo}.."
+        assert max_abs(head_block(lse[..., None], lo, lo + 8)[..., 0], L_ref) <= L_TOL, \
+            f"L, heads {lo}.."
 
 
 @pytest.mark.parametrize("causal", [False, True, "offset"])
