@@ -2,14 +2,27 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-Default workload: the non-causal prefill forward, B=4, H=16, Nq=Nk=2048,
-d=64, bf16 (one step = one fa_fwd over the whole batch, inputs resident in
-HBM).  It prints ONE JSON line whose ``value`` is that forward's throughput in
-TFLOP/s (4*B*H*Nq*Nk*d per step, halved under causal).  The same line carries
-``roofline`` for the dominant kernel, ``cpu_baseline`` (the fp64 oracle timed
-on a bounded sample on this host) and ``parts``: the causal d=128 prefill
-forward, the causal backward (10*B*H*N^2*d/2 per step) and split-KV decoding
-(GB/s of K, V, Q, O and L), each timed the same way.
+Default workload: the causal prefill forward, B=1, H=32, Nq=Nk=8192, d=128,
+bf16, one K row per head scaled by 30 (the largest workload; one step = one
+fa_fwd over the whole batch, inputs resident in HBM).  It prints ONE JSON line
+whose ``value`` is that forward's throughput in TFLOP/s (4*B*H*Nq*Nk*d per
+step, halved under causal).  ``parts`` holds the other workloads measured the
+same way: the non-causal d=64 prefill forward, the causal backward
+(10*B*H*N^2*d/2 per step) and split-KV decoding (GB/s of K, V, Q, O and L).
+
+Every workload, the primary one and each part, carries
+  roofline      its dominant kernel against the published peak: achieved
+                work per launch / launch time (HIP events on the launch
+                stream), HBM traffic from the committed counter profile while
+                the kernel source is unchanged, the sustained shader clock,
+                and the median and minimum over repeated timed regions;
+  cpu_baseline  the fp64 oracle timed on this host on a bounded sample of the
+                same inputs, in the workload's unit (forward: the dense
+                definition and the online recurrence with 64-key blocks;
+                backward: the dense Jacobian backward; decode: the dense
+                definition and split-and-merge), with the thread count used;
+  parity        the largest errors of the GPU result against the oracle on
+                that sample, beside the tolerances.
 
 After each workload is timed it keeps running back to back for --clock-s
 seconds while a thread reads the shader clock the driver reports
@@ -70,12 +83,17 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--settle", type=float, default=0.3,
                    help="keep warming up (untimed) until this many seconds have passed")
-    p.add_argument("--workload", default="prefill_d64",
+    p.add_argument("--workload", default="prefill_causal_d128",
                    choices=["prefill_d64", "prefill_causal_d128", "bwd_causal_d64",
                             "decode_d128"])
     p.add_argument("--n-split", type=int, default=None, help="decode: splits (default best)")
     p.add_argument("--no-parts", action="store_true", help="time only the primary workload")
-    p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    p.add_argument("--no-cpu", action="store_true",
+                   help="skip the oracle baseline and the parity sample")
+    p.add_argument("--cpu-budget", type=float, default=3.0,
+                   help="seconds of oracle work per routine and workload (bounded sample)")
+    p.add_argument("--repeats", type=int, default=5,
+                   help="timed regions of K steps per workload for the median and minimum")
     p.add_argument("--clock-s", type=float, default=1.5,
                    help="seconds of extra steps per workload while the clock is sampled (0: off)")
     p.add_argument("--copy-calibration", action="store_true")
@@ -105,7 +123,7 @@ def setup(name, fa, torch, n_split=None):
             fa.fa_fwd(x.q, x.k, x.v, o, lse, scale, causal)
         flops = 4.0 * B * H * Nq * Nk * d * (0.5 if causal else 1.0)
         return dict(step=step, work=flops, unit="TFLOP/s", bound="mfma", cfg=cfg, x=x,
-                    scale=scale, causal=causal, kernel="fwd_bf16_kernel")
+                    scale=scale, causal=causal, kernel="fwd_bf16_kernel", out=dict(o=o, lse=lse))
     if name.startswith("bwd"):
         o, lse = fa.forward(x.q, x.k, x.v, scale, causal)
         ws = torch.empty(fa.fa_bwd_workspace_size(x.q.dtype, B, H, Nq, d), dtype=torch.uint8,
@@ -116,7 +134,8 @@ def setup(name, fa, torch, n_split=None):
             fa.fa_bwd(x.q, x.k, x.v, o, lse, x.do, dq, dk, dv, ws, scale, causal)
         flops = 10.0 * B * H * Nq * Nk * d * (0.5 if causal else 1.0)
         return dict(step=step, work=flops, unit="TFLOP/s", bound="mfma", cfg=cfg, x=x,
-                    scale=scale, causal=causal, kernel="bwd_main_kernel",
+                    scale=scale, causal=causal, kernel="bwd_dkdv_kernel",
+                    out=dict(dq=dq, dk=dk, dv=dv),
                     extra={"flops_no_recompute": 8.0 * B * H * Nq * Nk * d * 0.5})
     # decode
     splits = [n_split] if n_split else list(w["n_split"])
@@ -134,6 +153,7 @@ def setup(name, fa, torch, n_split=None):
     bytes_ = 2.0 * (2 * B * H * Nk * d + 2 * B * H * Nq * d) + 4.0 * B * H * Nq
     return dict(step=step, work=bytes_, unit="GB/s", bound="hbm", cfg=cfg, x=x, scale=scale,
                 causal=False, kernel="decode_split_kernel", splits=splits, state=state,
+                out=dict(o=o, lse=lse),
                 partial_bytes={n: 4.0 * B * H * Nq * n * (d + 2) * 2 for n in splits})
 
 
@@ -301,39 +321,123 @@ def io_model(run, fa_mod):
     return out
 
 
-def cpu_baseline(run, budget_s=12.0):
-    """The fp64 oracle (dense definition) on a bounded sample of query rows of
-    the same inputs, in the metric's unit."""
+def _timed_oracle(fn):
+    t0 = time.perf_counter()
+    out = fn()
+    return out, time.perf_counter() - t0
+
+
+def _grow(n, total, dt, budget_s):
+    """Sample size for the next try: aim at the budget, at least double."""
+    return int(min(total, n * max(2.0, budget_s / max(dt, 1e-3))))
+
+
+def oracle_leg(run, budget_s):
+    """The fp64 oracle on a bounded sample of the same inputs: its speed on
+    this host in the workload's unit (``cpu_baseline``) and the largest errors
+    of the GPU result against it on that sample (``parity``).  The sample
+    grows until one routine takes about a quarter of ``budget_s``."""
     import numpy as np
     import oracle
     from fa_inputs import to_f64_numpy
-    x = run["x"]
+    threads = oracle.default_threads()
+    x, out = run["x"], run["out"]
     B, H, Nq, d = x.q.shape
     Nk = x.k.shape[2]
-    Q, K, V = (to_f64_numpy(t) for t in (x.q, x.k, x.v))
-    threads = oracle.default_threads()
+    scale, causal = run["scale"], run["causal"]
     rng = np.random.default_rng(0)
-    total = B * H * Nq
-    n = min(total, 256)
-    spent = 0.0
-    work = 0.0
-    while True:
-        rows = np.sort(rng.choice(total, size=n, replace=False))
-        t0 = time.perf_counter()
-        oracle.dense_fwd(Q, K, V, run["scale"], run["causal"], rows=rows, nthreads=threads)
-        dt = time.perf_counter() - t0
-        if run["causal"]:
-            vis = np.minimum(rows % Nq + 1, Nk)
-        else:
-            vis = np.full(rows.shape, Nk)
+    routines = {}
+
+    def entry(name, work, dt, unit_scale):
+        routines[name] = {"value": round(work / dt / unit_scale, 6), "seconds": round(dt, 3)}
+
+    if run["cfg"]["workload"].startswith("prefill"):
+        Q, K, V = (to_f64_numpy(t) for t in (x.q, x.k, x.v))
+        total = B * H * Nq
+        n = min(total, 64)
+        while True:
+            rows = np.sort(rng.choice(total, size=n, replace=False))
+            (O1, L1), dt1 = _timed_oracle(lambda: oracle.dense_fwd(
+                Q, K, V, scale, causal, rows=rows, nthreads=threads))
+            if dt1 > budget_s / 4 or n == total:
+                break
+            n = _grow(n, total, dt1, budget_s)
+        (O2, L2), dt2 = _timed_oracle(lambda: oracle.online_fwd(
+            Q, K, V, scale, causal, block=64, rows=rows, nthreads=threads))
+        vis = np.minimum(rows % Nq + 1, Nk) if causal else np.full(rows.shape, Nk)
         work = float(4.0 * d * vis.sum())
-        spent = dt
-        if dt > budget_s / 4 or n == total:
-            break
-        n = int(min(total, n * max(2.0, budget_s / 2 / max(dt, 1e-3))))
-    value = work / spent / 1e12
-    return {"value": round(value, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {total} query rows (dense fp64 definition), {spent:.2f} s"}
+        entry("dense_definition", work, dt1, 1e12)
+        entry("online_block64", work, dt2, 1e12)
+        go = to_f64_numpy(out["o"]).reshape(-1, d)[rows]
+        gl = to_f64_numpy(out["lse"]).reshape(-1)[rows]
+        parity = {"sample": f"{rows.size} of {total} query rows",
+                  "o_max_abs": float(np.abs(go - O1).max()), "o_tol": 2e-2,
+                  "l_max_abs": float(np.abs(gl - L1).max()), "l_tol": 1e-3,
+                  "online_vs_dense_max_abs": float(max(np.abs(O2 - O1).max(),
+                                                       np.abs(L2 - L1).max()))}
+        parity["ok"] = parity["o_max_abs"] <= 2e-2 and parity["l_max_abs"] <= 1e-3
+        sample = f"{rows.size} of {total} query rows"
+        unit = "TFLOP/s"
+    elif run["cfg"]["workload"].startswith("bwd"):
+        heads_all = rng.permutation(B * H)
+        nh = min(B * H, threads)
+        while True:
+            heads = np.sort(heads_all[:nh])
+            sl = lambda t: to_f64_numpy(t.reshape(B * H, -1, d)[heads])[None]
+            Q, K, V, dO = (sl(t) for t in (x.q, x.k, x.v, x.do))
+            g, dt = _timed_oracle(lambda: oracle.dense_bwd(Q, K, V, dO, scale, causal,
+                                                           nthreads=threads))
+            if dt > budget_s / 4 or nh == B * H:
+                break
+            nh = min(B * H, nh * 2)
+        work = 10.0 * nh * Nq * Nk * d * (0.5 if causal else 1.0)
+        entry("dense_jacobian_backward", work, dt, 1e12)
+        parity = {"sample": f"{nh} of {B * H} heads, every element"}
+        ok = True
+        for key, t in (("dQ", out["dq"]), ("dK", out["dk"]), ("dV", out["dv"])):
+            got = to_f64_numpy(t.reshape(B * H, -1, d)[heads])
+            ref = g[key][0]
+            rel = float(np.abs(got - ref).max() / np.abs(ref).max())
+            parity[f"{key}_max_rel"] = rel
+            ok = ok and rel <= 5e-2
+        parity["tol_max_rel"] = 5e-2
+        parity["ok"] = ok
+        sample = f"{nh} of {B * H} heads (whole heads)"
+        unit = "TFLOP/s"
+    else:
+        n_split = run["state"]["n"]
+        total = B * H * Nq
+        cap = min(total, 64)  # rows whose whole K/V cache (64 MiB fp64 each) comes to the host
+        n = min(cap, 16)
+        while True:
+            heads = np.sort(rng.choice(B * H, size=n, replace=False))
+            sl = lambda t: to_f64_numpy(t.reshape(B * H, -1, d)[heads])[None]
+            Q, K, V = (sl(t) for t in (x.q, x.k, x.v))
+            (O1, L1), dt1 = _timed_oracle(lambda: oracle.dense_fwd(Q, K, V, scale,
+                                                                   nthreads=threads))
+            if dt1 > budget_s / 4 or n == cap:
+                break
+            n = _grow(n, cap, dt1, budget_s)
+        (O6, L6, _, _, _), dt6 = _timed_oracle(lambda: oracle.split_decode(
+            Q, K, V, n_split, scale, nthreads=threads))
+        per_row = 2.0 * (2 * Nk * d + 2 * d) + 4.0
+        entry("dense_definition", per_row * n, dt1, 1e9)
+        entry(f"split_merge_{n_split}", per_row * n, dt6, 1e9)
+        go = to_f64_numpy(out["o"]).reshape(B * H, d)[heads]
+        gl = to_f64_numpy(out["lse"]).reshape(B * H)[heads]
+        parity = {"sample": f"{n} of {B * H} heads, n_split {n_split}",
+                  "o_max_abs": float(np.abs(go - O1.reshape(n, d)).max()), "o_tol": 2e-2,
+                  "l_max_abs": float(np.abs(gl - L1.reshape(n)).max()), "l_tol": 1e-3,
+                  "split_vs_dense_max_abs": float(max(np.abs(O6 - O1.reshape(O6.shape)).max(),
+                                                      np.abs(L6 - L1.reshape(L6.shape)).max()))}
+        parity["ok"] = parity["o_max_abs"] <= 2e-2 and parity["l_max_abs"] <= 1e-3
+        sample = f"{n} of {total} query rows (whole K/V cache of each)"
+        unit = "GB/s"
+    first = next(iter(routines.values()))
+    cpu = {"value": first["value"], "unit": unit, "cores": threads, "kind": "oracle",
+           "sample": sample + f"; {next(iter(routines))}, {first['seconds']:.2f} s",
+           "routines": routines}
+    return cpu, parity
 
 
 def copy_calibration(torch):
@@ -381,6 +485,58 @@ def sweep(torch, fa, steps, warmup, settle_s):
             torch.cuda.empty_cache()
 
 
+def repeated(torch, step, steps, repeats):
+    """Median and minimum ms per step over `repeats` further timed regions of
+    `steps` steps each (the clock has settled by then)."""
+    if repeats <= 0:
+        return None
+    stream = torch.cuda.current_stream()
+    ms = []
+    for _ in range(repeats):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(steps):
+            step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b) / steps)
+    ms.sort()
+    return {"regions": repeats, "steps": steps, "median_ms": round(ms[len(ms) // 2], 5),
+            "min_ms": round(ms[0], 5)}
+
+
+def measure_workload(name, fa, torch, args, steps, warmup, n_split=None):
+    """Time one workload and gather its roofline, oracle baseline and parity
+    sample.  Returns (ms per step of the first timed region, entry dict)."""
+    run = setup(name, fa, torch, n_split)
+    ms = measure(run, torch, steps, warmup, args.settle)
+    rf = roofline(run, ms, name)
+    rep = repeated(torch, run["step"], steps, args.repeats)
+    if rep:
+        rf["repeats"] = rep
+        rf["frac_median"] = round(run["work"] / rep["median_ms"] /
+                                  (1e9 if run["unit"] == "TFLOP/s" else 1e6) / rf["peak"], 4)
+    add_clock(rf, run, sample_clock(torch, run["step"], args.clock_s))
+    if run["kernel"] == "fwd_bf16_kernel":
+        rf["io_flash"] = io_model(run, fa)
+    cfg = dict(run["cfg"])
+    if "partial_bytes" in run:
+        cfg["partial_state_bytes"] = run["partial_bytes"][run["state"]["n"]]
+    if "extra" in run:
+        cfg.update(run["extra"])
+    entry = {"ms": round(ms, 5), "value": round(rate(run, ms), 3),
+             "unit": run["unit"] if run["unit"] == "TFLOP/s" else "GB/s", "config": cfg,
+             "roofline": rf}
+    if not args.no_cpu:
+        torch.cuda.synchronize()
+        entry["cpu_baseline"], entry["parity"] = oracle_leg(run, args.cpu_budget)
+    del run
+    torch.cuda.empty_cache()
+    return ms, entry
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -396,51 +552,28 @@ def main():
     if args.sweep:
         sweep(torch, fa, args.steps, args.warmup, args.settle)
         return
-    run = setup(args.workload, fa, torch, args.n_split)
-    ms = measure(run, torch, args.steps, args.warmup, args.settle)
-    value = rate(run, ms)
+    ms, prim = measure_workload(args.workload, fa, torch, args, args.steps, args.warmup,
+                                args.n_split)
     line = {
         "metric": "attention TFLOP/s and % of bf16 MFMA peak (fwd/bwd); decode GB/s % HBM peak",
-        "value": round(value, 3),
-        "unit": run["unit"] if run["unit"] == "TFLOP/s" else "GB/s",
+        "value": prim["value"],
+        "unit": prim["unit"],
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "warmup_settle_s": args.settle,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": run["cfg"],
-        "roofline": roofline(run, ms, args.workload),
+        "config": prim["config"],
+        "roofline": prim["roofline"],
     }
-    add_clock(line["roofline"], run, sample_clock(torch, run["step"], args.clock_s))
-    if run["kernel"] == "fwd_bf16_kernel":
-        line["roofline"]["io_flash"] = io_model(run, fa)
-    if "partial_bytes" in run:
-        line["config"]["partial_state_bytes"] = run["partial_bytes"][run["state"]["n"]]
-    if "extra" in run:
-        line["config"].update(run["extra"])
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(run) if run["unit"] == "TFLOP/s" else None
-    primary_x = run.pop("x")
-    del primary_x
+        line["cpu_baseline"] = prim["cpu_baseline"]
+        line["parity"] = prim["parity"]
     if not args.no_parts:
         parts = {}
-        for name in ("prefill_d64", "prefill_causal_d128", "bwd_causal_d64", "decode_d128"):
+        for name in ("prefill_causal_d128", "prefill_d64", "bwd_causal_d64", "decode_d128"):
             if name == args.workload:
                 continue
-            r = setup(name, fa, torch)
             steps = max(3, args.steps // 2) if name == "decode_d128" else args.steps
-            pms = measure(r, torch, steps, min(args.warmup, 3), args.settle)
-            rf = roofline(r, pms, name)
-            add_clock(rf, r, sample_clock(torch, r["step"], args.clock_s))
-            parts[name] = {"ms": round(pms, 5), "value": round(rate(r, pms), 3),
-                           "unit": rf["unit"], "frac": rf["frac"], "traffic": rf["traffic"],
-                           "sclk_mhz": rf["sclk_mhz"], "config": r["cfg"]}
-            if "frac_at_sclk" in rf:
-                parts[name]["frac_at_sclk"] = rf["frac_at_sclk"]
-            if r["kernel"] == "fwd_bf16_kernel":
-                parts[name]["io_flash"] = io_model(r, fa)
-            if "partial_bytes" in r:
-                parts[name]["partial_state_bytes"] = r["partial_bytes"][r["state"]["n"]]
-            del r
-            torch.cuda.empty_cache()
+            _, parts[name] = measure_workload(name, fa, torch, args, steps, min(args.warmup, 3))
         line["parts"] = parts
     print(json.dumps(line), flush=True)
 

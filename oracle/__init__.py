@@ -54,8 +54,8 @@ def _lib():
                                          _i64, ctypes.c_double, ctypes.c_int, _i64, _ip, _i64,
                                          ctypes.c_int]
         lib.oracle_online_fwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, _i64,
-                                          _i64, ctypes.c_double, ctypes.c_int, _i64, _i64,
-                                          ctypes.c_int]
+                                          _i64, ctypes.c_double, ctypes.c_int, _i64, _i64, _ip,
+                                          _i64, ctypes.c_int]
         lib.oracle_dense_bwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64,
                                          _i64, _i64, _i64, _i64, _i64, ctypes.c_double,
                                          ctypes.c_int, _i64, _ip, _i64, ctypes.c_int]
@@ -132,19 +132,26 @@ def dense_fwd(Q, K, V, scale: float, causal: bool = False, q_start: int = 0, row
 
 
 def online_fwd(Q, K, V, scale: float, causal: bool = False, block: int = 64, q_start: int = 0,
-               nthreads: int | None = None):
+               rows=None, nthreads: int | None = None):
     """Per-row online softmax over key blocks of ``block`` (tiled in lab.py;
     TiledAttention in model.py; flash_forward in attention_kernels.py).
-    Returns (O, L) like dense_fwd."""
+    Returns (O, L) like dense_fwd, ``rows`` included."""
     Q, K, V = _f64(Q), _f64(K), _f64(V)
     _check4(Q, K, V)
     B, H, Nq, d = Q.shape
     Nk, dv = K.shape[2], V.shape[3]
-    O = np.empty((B, H, Nq, dv))
-    L = np.empty((B, H, Nq))
+    if rows is None:
+        O = np.empty((B, H, Nq, dv))
+        L = np.empty((B, H, Nq))
+        rp, nr = None, 0
+    else:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        O = np.empty((rows.size, dv))
+        L = np.empty(rows.size)
+        rp, nr = rows.ctypes.data_as(_ip), rows.size
     st = _lib().oracle_online_fwd(_p(Q), _p(K), _p(V), _p(O), _p(L), B, H, Nq, Nk, d, dv,
                                   float(scale), int(bool(causal)), int(q_start), int(block),
-                                  nthreads or default_threads())
+                                  rp, nr, nthreads or default_threads())
     if st == 2:
         raise ValueError("block must be >= 1")
     if st != 0:

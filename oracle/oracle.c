@@ -173,19 +173,19 @@ int oracle_dense_fwd(const double *Q, const double *K, const double *V, double *
 static void online_row(void *vctx, int64_t item)
 {
     struct fwd_args *a = (struct fwd_args *)vctx;
-    int64_t row = item;
+    int64_t row = a->rows ? a->rows[item] : item;
     int64_t bh = row / a->Nq, i = row % a->Nq;
     const double *q = a->Q + row * a->d;
     const double *K = a->K + bh * a->Nk * a->d;
     const double *V = a->V + bh * a->Nk * a->dv;
-    double *o = a->O + row * a->dv;
+    double *o = a->O + item * a->dv;
     /* The visible keys are the prefix 0 .. nvis-1; it is cut into blocks of
      * `block` keys (the last one shorter), visited in order. */
     int64_t nvis = visible_keys(i, a->Nk, a->causal, a->q_start);
     if (nvis == 0) {
         a->status = 1;
         for (int64_t c = 0; c < a->dv; ++c) o[c] = NAN;
-        a->L[row] = NAN;
+        a->L[item] = NAN;
         return;
     }
     double *num = (double *)calloc((size_t)a->dv, sizeof(double));
@@ -217,18 +217,21 @@ static void online_row(void *vctx, int64_t item)
         m = m_new;
     }
     for (int64_t c = 0; c < a->dv; ++c) o[c] = num[c] / l;
-    a->L[row] = m + log(l);
+    a->L[item] = m + log(l);
     free(num);
     free(s);
 }
 
+/* All rows when rows == NULL, else the listed flat rows packed in list order
+ * (as oracle_dense_fwd). */
 int oracle_online_fwd(const double *Q, const double *K, const double *V, double *O, double *L,
                       int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv,
-                      double scale, int causal, int64_t q_start, int64_t block, int nthreads)
+                      double scale, int causal, int64_t q_start, int64_t block,
+                      const int64_t *rows, int64_t nrows, int nthreads)
 {
     if (block < 1) return 2;
-    struct fwd_args a = {Q, K, V, O, L, H, Nq, Nk, d, dv, scale, causal, q_start, NULL, block, 0};
-    parallel_for(B * H * Nq, nthreads, online_row, &a);
+    struct fwd_args a = {Q, K, V, O, L, H, Nq, Nk, d, dv, scale, causal, q_start, rows, block, 0};
+    parallel_for(rows ? nrows : B * H * Nq, nthreads, online_row, &a);
     return a.status;
 }
 

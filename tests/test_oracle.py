@@ -145,6 +145,17 @@ def test_dense_invariants(causal):
                 assert np.all(O[b, h, i] <= V[b, h, :nv].max(0) + 1e-12)
 
 
+def test_online_rows_subset():
+    """The online routine on listed rows returns exactly those rows of the
+    whole computation, in list order."""
+    Q, K, V = (_rand((2, 3, 21, 5), 60 + t) for t in range(3))
+    O, L = oracle.online_fwd(Q, K, V, 0.4, True, block=4)
+    rows = np.array([17, 0, 125, 64, 3])
+    Or, Lr = oracle.online_fwd(Q, K, V, 0.4, True, block=4, rows=rows)
+    np.testing.assert_array_equal(Or, O.reshape(-1, 5)[rows])
+    np.testing.assert_array_equal(Lr, L.reshape(-1)[rows])
+
+
 def test_dense_rows_subset():
     """The row-sampled entry returns exactly the full rows it names."""
     Q, K, V = _rand((2, 3, 20, 8), 21), _rand((2, 3, 25, 8), 22), _rand((2, 3, 25, 8), 23)
