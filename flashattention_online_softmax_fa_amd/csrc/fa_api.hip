@@ -333,6 +333,7 @@ const char *fa_status_str(fa_status s) {
         case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
         case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
         case FA_ERR_HIP: return "FA_ERR_HIP";
+        default: break;
     }
     return "FA_ERR_UNKNOWN";
 }

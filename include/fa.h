@@ -56,12 +56,14 @@ typedef enum fa_status {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, size < 1, bad scale, ... */
     FA_ERR_UNSUPPORTED = 2, /* valid request outside what is built (d, dtype)   */
-    FA_ERR_HIP = 3          /* the HIP runtime refused a launch                  */
+    FA_ERR_HIP = 3,         /* the HIP runtime refused a launch                  */
+    FA_STATUS_INT = 0x7fffffff /* not a status: makes every int a valid value    */
 } fa_status;
 
 typedef enum fa_dtype {
     FA_F32 = 0,  /* IEEE binary32 */
-    FA_BF16 = 1  /* bfloat16      */
+    FA_BF16 = 1, /* bfloat16      */
+    FA_DTYPE_INT = 0x7fffffff /* not a dtype: makes every int a valid value (rejected) */
 } fa_dtype;
 
 /*
