@@ -90,7 +90,7 @@ def parse():
     p.add_argument("--no-parts", action="store_true", help="time only the primary workload")
     p.add_argument("--no-cpu", action="store_true",
                    help="skip the oracle baseline and the parity sample")
-    p.add_argument("--cpu-budget", type=float, default=3.0,
+    p.add_argument("--cpu-budget", type=float, default=6.0,
                    help="seconds of oracle work per routine and workload (bounded sample)")
     p.add_argument("--repeats", type=int, default=5,
                    help="timed regions of K steps per workload for the median and minimum")
