@@ -23,6 +23,8 @@
 // Both rings are filled with global_load_lds_dwordx4 into row-major,
 // chunk-swizzled tiles (see fa_device.h); a ring of 2*GR slots takes one
 // barrier per GR tiles (GR tiles computed on while the next GR are in flight).
+// With eight waves the two waves of a SIMD take turns issuing both their
+// shares of the loads (FA_BWD_DMA_ALT), as in the forward.
 //
 // Layouts (v_mfma_f32_32x32x16_bf16, C[m][n] with lane = n):
 //   dkdv: S = Q K^T and dP = dO V^T put one KEY per lane, so P and dS are
@@ -35,6 +37,14 @@
 #include "fa_internal.h"
 
 #include <type_traits>
+
+// 1: at each barrier of a pass with eight waves, only one wave of each SIMD's
+// pair (waves w and w ^ 4) issues the next group's ring loads, for both,
+// alternating between the two from one barrier to the next: its partner
+// computes meanwhile instead of queueing for the loads.
+#ifndef FA_BWD_DMA_ALT
+#define FA_BWD_DMA_ALT 1
+#endif
 
 namespace fa {
 namespace {
@@ -133,45 +143,53 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     // ring loads: this lane fills chunk `lane` of its IPW 1 KiB blocks of the
     // Q and dO tiles (row (wave*IPW + u)*RPI + lane/CH of the tile, logical
     // chunk (lane % CH) ^ swz(row)); waves 0 and 1 also fill the L2 and D slices
-    auto ld_row = [&](int u) { return (wave * T::IPW + u) * T::RPI + lane / T::CH; };
-    uint32_t ld_off[T::IPW];  // byte offset of this lane's load within a tile
-#pragma unroll
-    for (int u = 0; u < T::IPW; ++u) ld_off[u] = (uint32_t)chunk_off<ROWB>(ld_row(u), lane % T::CH);
-    // LDS destinations as scalar byte addresses: this wave's first block in
-    // stage 0, and its L2 / D slice (waves 0 and 1)
+    //      (with FA_BWD_DMA_ALT, also those of the partner wave w ^ 4)
+    constexpr bool ALT = FA_BWD_DMA_ALT && W == 8 && GR > 1;
     const uint32_t wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t lds_w = lds_addr(smem) + wave_u * (T::IPW * 1024);
-    const uint32_t lds_v = lds_addr(smem) + 2 * T::TILEB + wave_u * T::VECB;
-    auto issue = [&](int it, int st) {
+    const uint32_t owner_u[2] = {wave_u, wave_u ^ 4u};
+    auto ld_row = [&](int o, int u) { return ((int)owner_u[o] * T::IPW + u) * T::RPI + lane / T::CH; };
+    uint32_t ld_off[2][T::IPW];  // byte offset of this lane's load within a tile
+#pragma unroll
+    for (int o = 0; o < (ALT ? 2 : 1); ++o)
+#pragma unroll
+        for (int u = 0; u < T::IPW; ++u)
+            ld_off[o][u] = (uint32_t)chunk_off<ROWB>(ld_row(o, u), lane % T::CH);
+    // the loads of wave owner_u[o] for query tile it into stage st; LDS
+    // destinations as scalar byte addresses: that wave's first block in the
+    // stage, and its L2 / D slice (waves 0 and 1)
+    auto issue_as = [&](int it, int st, int o) {
+        const uint32_t ow = owner_u[o];
         const int64_t q0 = (int64_t)it * BR;
-        const uint32_t qb = lds_w + st * T::STAGEB, ob = qb + T::TILEB;
-        const uint32_t vb = lds_v + st * T::STAGEB;
+        const uint32_t qb = lds_addr(smem) + ow * (T::IPW * 1024) + st * T::STAGEB;
+        const uint32_t ob = qb + T::TILEB;
+        const uint32_t vb = lds_addr(smem) + 2 * T::TILEB + ow * T::VECB + st * T::STAGEB;
         if (q0 + 64 <= Nq) {  // every row and vector lane below in range: scalar bases
             const uint8_t *qs = (const uint8_t *)(Qh + q0 * D);
             const uint8_t *os = (const uint8_t *)(dOh + q0 * D);
 #pragma unroll
             for (int u = 0; u < T::IPW; ++u) {
-                dma16_s(qs, ld_off[u], qb + u * 1024);
-                dma16_s(os, ld_off[u], ob + u * 1024);
+                dma16_s(qs, ld_off[o][u], qb + u * 1024);
+                dma16_s(os, ld_off[o][u], ob + u * 1024);
             }
-            if (wave_u < 2) dma4((wave_u == 0 ? L2h : Dh) + q0 + lane, vb);
+            if (ow < 2) dma4((ow == 0 ? L2h : Dh) + q0 + lane, vb);
             return;
         }
 #pragma unroll
         for (int u = 0; u < T::IPW; ++u) {
-            const int row = ld_row(u);
+            const int row = ld_row(o, u);
             const int64_t q = q0 + row < Nq ? q0 + row : Nq - 1;  // past the end: masked later
-            const uint8_t *src = (const uint8_t *)(Qh + q * D) + (ld_off[u] - row * ROWB);
-            const uint8_t *srco = (const uint8_t *)(dOh + q * D) + (ld_off[u] - row * ROWB);
+            const uint8_t *src = (const uint8_t *)(Qh + q * D) + (ld_off[o][u] - row * ROWB);
+            const uint8_t *srco = (const uint8_t *)(dOh + q * D) + (ld_off[o][u] - row * ROWB);
             dma16(src, qb + u * 1024);
             dma16(srco, ob + u * 1024);
         }
-        if (wave_u < 2) {
+        if (ow < 2) {
             int64_t q = q0 + lane;
             q = q < Nq ? q : Nq - 1;
-            dma4((wave_u == 0 ? L2h : Dh) + q, vb);
+            dma4((ow == 0 ? L2h : Dh) + q, vb);
         }
     };
+    auto issue = [&](int it, int st) { issue_as(it, st, 0); };
 
     int roff[D / 16], toff[D / 32];
 #pragma unroll
@@ -309,9 +327,14 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         if (idx % GR == 0) {
             wait_vm<0>();
             lds_barrier();
+            if (!ALT || ((idx / GR) & 1) == (int)(wave_u >> 2)) {
 #pragma unroll
-            for (int t = GR; t < 2 * GR; ++t)
-                if (it + t < nqt) issue(it + t, (idx + t) % ST);
+                for (int t = GR; t < 2 * GR; ++t)
+                    if (it + t < nqt) {
+                        issue_as(it + t, (idx + t) % ST, 0);
+                        if (ALT) issue_as(it + t, (idx + t) % ST, 1);
+                    }
+            }
         }
         const int64_t q0 = (int64_t)it * BR;
         const int64_t q_last = (q0 + BR < Nq ? q0 + BR : Nq) - 1;  // last real query of the tile
@@ -452,11 +475,17 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
         dq[qb] = qrow < Nq ? dsum : 0.f;
     }
 
-    auto ld_row = [&](int u) { return (wave * T::IPW + u) * T::RPI + lane / T::CH; };
-    uint32_t ld_off[T::IPW];  // byte offset of this lane's load within a tile
+    constexpr bool ALT = FA_BWD_DMA_ALT && W == 8 && GR > 1;
+    const int owner[2] = {wave, wave ^ 4};  // this wave and, with ALT, its partner
+    auto ld_row = [&](int o, int u) { return (owner[o] * T::IPW + u) * T::RPI + lane / T::CH; };
+    uint32_t ld_off[2][T::IPW];  // byte offset of this lane's load within a tile
 #pragma unroll
-    for (int u = 0; u < T::IPW; ++u) ld_off[u] = (uint32_t)chunk_off<ROWB>(ld_row(u), lane % T::CH);
-    auto issue = [&](int64_t j, int st) {
+    for (int o = 0; o < (ALT ? 2 : 1); ++o)
+#pragma unroll
+        for (int u = 0; u < T::IPW; ++u)
+            ld_off[o][u] = (uint32_t)chunk_off<ROWB>(ld_row(o, u), lane % T::CH);
+    // the loads of wave owner[o] for key tile j into stage st
+    auto issue_as = [&](int64_t j, int st, int o) {
         const int64_t kv0 = j * BC;
         uint8_t *kb = smem + st * 2 * T::TILEB;
         uint8_t *vb = kb + T::TILEB;
@@ -465,22 +494,23 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
             const uint8_t *vs = (const uint8_t *)(Vh + kv0 * D);
 #pragma unroll
             for (int u = 0; u < T::IPW; ++u) {
-                const int blk = wave * T::IPW + u;
-                dma16_s(ks, ld_off[u], kb + blk * 1024);
-                dma16_s(vs, ld_off[u], vb + blk * 1024);
+                const int blk = owner[o] * T::IPW + u;
+                dma16_s(ks, ld_off[o][u], kb + blk * 1024);
+                dma16_s(vs, ld_off[o][u], vb + blk * 1024);
             }
             return;
         }
 #pragma unroll
         for (int u = 0; u < T::IPW; ++u) {
-            const int row = ld_row(u);
+            const int row = ld_row(o, u);
             const int64_t key = kv0 + row < Nk ? kv0 + row : Nk - 1;  // past the end: masked
-            const uint32_t col = ld_off[u] - row * ROWB;
-            const int blk = wave * T::IPW + u;
+            const uint32_t col = ld_off[o][u] - row * ROWB;
+            const int blk = owner[o] * T::IPW + u;
             dma16((const uint8_t *)(Kh + key * D) + col, kb + blk * 1024);
             dma16((const uint8_t *)(Vh + key * D) + col, vb + blk * 1024);
         }
     };
+    auto issue = [&](int64_t j, int st) { issue_as(j, st, 0); };
     int koff[D / 16], toff[D / 32];
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) koff[ds] = chunk_off<ROWB>(lr, 2 * ds + g);
@@ -579,9 +609,13 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
         if (j % GR != 0) return;  // one barrier per GR tiles, as in the dK/dV pass
         wait_vm<0>();
         lds_barrier();
+        if (ALT && ((j / GR) & 1) != (wave >> 2)) return;
 #pragma unroll
         for (int t = GR; t < 2 * GR; ++t)
-            if (j + t < nkt) issue(j + t, (int)((j + t) % ST));
+            if (j + t < nkt) {
+                issue_as(j + t, (int)((j + t) % ST), 0);
+                if (ALT) issue_as(j + t, (int)((j + t) % ST), 1);
+            }
     };
     // leading tiles with every key visible to every query of this wave
     int64_t nfull = 0;

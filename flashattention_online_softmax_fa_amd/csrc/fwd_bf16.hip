@@ -10,8 +10,13 @@
 // Work split.  One workgroup (W waves) per (batch*head, query tile); each
 // wave owns 32*QB queries, whose Q rows stay in registers.  Key/value tiles of
 // BC keys stream from HBM straight into an LDS ring of STAGES slots with
-// global_load_lds_dwordx4 (no register staging); each wave issues its share of
-// a tile and waits on its own load counter.  One barrier per GR tiles both
+// global_load_lds_dwordx4 (no register staging); the loads of a tile are split
+// over the waves, each waiting on its own load counter.  With eight waves the
+// two waves of a SIMD (w and w ^ 4) take turns, one barrier to the next, to
+// issue both their shares: issued by every wave right after the barrier, the
+// loads queue in the CU's one address unit while the SIMDs idle, and a
+// per-wave timeline put that queueing at 15 % of the d = 128 key loop.  One
+// barrier per GR tiles both
 // publishes the next GR tiles and frees the GR slots read in the steps before
 // it, which are refilled right away (so GR tiles are in flight while GR are
 // computed on; fewer barriers per key: d = 64 takes GR = 4 with a 16-slot
@@ -74,6 +79,12 @@
 #ifndef FA_FWD_GR64  // key tiles per LDS barrier (the ring depth must be >= 2 * this + 1)
 #define FA_FWD_GR64 4
 #define FA_FWD_GR128 2
+#endif
+// 1: at each barrier only one wave of each SIMD's pair (waves w and w ^ 4)
+// issues the group's ring loads, for both waves, alternating between the two
+// from one barrier to the next
+#ifndef FA_FWD_DMA_ALT
+#define FA_FWD_DMA_ALT 1
 #endif
 
 namespace fa {
@@ -163,33 +174,41 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     // ---- ring loads: load j = wave * LPW + u of a step fills 1 KiB block j % NB
     //      of the K (j < NB) or V tile; this lane writes LDS chunk `lane` of the
     //      block with logical chunk (lane % CH) ^ f(row) of that row
-    int ld_row[T::LPW], ld_off[T::LPW];
+    //      (and, with FA_FWD_DMA_ALT, the same for the partner wave w ^ 4)
+    constexpr bool ALT = FA_FWD_DMA_ALT && W == 8 && GR > 1;
+    const int partner = wave ^ 4;
+    int ld_row[2][T::LPW], ld_off[2][T::LPW];
 #pragma unroll
-    for (int u = 0; u < T::LPW; ++u) {
-        const int row = ((wave * T::LPW + u) % T::NB) * T::RPI + lane / T::CH;
-        ld_row[u] = row;
-        ld_off[u] = chunk_off<T::ROWB>(row, lane % T::CH);
-    }
-    auto issue = [&](int t, int st) {
+    for (int o = 0; o < (ALT ? 2 : 1); ++o)
+#pragma unroll
+        for (int u = 0; u < T::LPW; ++u) {
+            const int row = (((o ? partner : wave) * T::LPW + u) % T::NB) * T::RPI + lane / T::CH;
+            ld_row[o][u] = row;
+            ld_off[o][u] = chunk_off<T::ROWB>(row, lane % T::CH);
+        }
+    // the loads of wave `owner` (0: this wave, 1: its partner) for tile t into slot st
+    auto issue_as = [&](int t, int st, int owner) {
         const int64_t kv0 = (int64_t)t * BC;
         const uint8_t *kt = (const uint8_t *)(Kh + kv0 * D);
         const uint8_t *vt = (const uint8_t *)(Vh + kv0 * D);
         const bool full = kv0 + BC <= Nk;
+        const int ow = owner ? partner : wave;
 #pragma unroll
         for (int u = 0; u < T::LPW; ++u) {
-            const int j = wave * T::LPW + u;  // wave-uniform
+            const int j = ow * T::LPW + u;  // wave-uniform
             const bool is_v = j >= T::NB;
             const uint8_t *src = is_v ? vt : kt;
             uint8_t *dst = smem + st * 2 * T::TILEB + j * 1024;  // V follows K in the slot
             if (full) {
-                dma16_s(src, (uint32_t)ld_off[u], dst);
+                dma16_s(src, (uint32_t)ld_off[owner][u], dst);
             } else {  // rows past Nk re-read the last key; they are masked
-                const int64_t key = kv0 + ld_row[u];
+                const int64_t key = kv0 + ld_row[owner][u];
                 const int64_t back = key < Nk ? 0 : (key - (Nk - 1)) * T::ROWB;
-                dma16(src + ld_off[u] - back, dst);
+                dma16(src + ld_off[owner][u] - back, dst);
             }
         }
     };
+    auto issue = [&](int t, int st) { issue_as(t, st, 0); };
     // wait until at most n ring steps of this wave's loads are still in flight
     auto wait_pending = [&](int n) { wait_steps<T::LPW, S - 2>(n); };
 
@@ -445,6 +464,18 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
             if (t % GR != 0) return;
             wait_vm<0>();
             lds_barrier();
+            if constexpr (ALT) {
+                // one wave of each SIMD's pair loads for both, in turn: its
+                // partner computes meanwhile instead of queueing for the loads
+                if (((t / GR) & 1) != (wave >> 2)) return;
+#pragma unroll
+                for (int j = GR + 1; j <= 2 * GR; ++j)
+                    if (t + j < nkt) {
+                        issue_as(t + j, (t + j) % S, 0);
+                        issue_as(t + j, (t + j) % S, 1);
+                    }
+                return;
+            }
 #pragma unroll
             for (int j = GR + 1; j <= 2 * GR; ++j)
                 if (t + j < nkt) issue(t + j, (t + j) % S);
