@@ -134,7 +134,8 @@ def setup(name, fa, torch, n_split=None):
             fa.fa_bwd(x.q, x.k, x.v, o, lse, x.do, dq, dk, dv, ws, scale, causal)
         flops = 10.0 * B * H * Nq * Nk * d * (0.5 if causal else 1.0)
         return dict(step=step, work=flops, unit="TFLOP/s", bound="mfma", cfg=cfg, x=x,
-                    scale=scale, causal=causal, kernel="bwd_dkdv_kernel",
+                    scale=scale, causal=causal,
+                    kernel="bwd_dkdv_pipe_kernel" if d == 64 else "bwd_dkdv_kernel",
                     out=dict(dq=dq, dk=dk, dv=dv),
                     extra={"flops_no_recompute": 8.0 * B * H * Nq * Nk * d * 0.5})
     # decode

@@ -16,10 +16,14 @@
 //                    of 32 queries, Q and dO in registers; K and V tiles of the key
 //                    tiles its queries can see stream through an LDS ring.  It
 //                    also forms D = rowsum(dO * O) and L2 = L * log2(e) of its
-//                    queries and writes them to the workspace;
+//                    queries and writes -D and L2 to the workspace;
 //   bwd_dkdv_kernel  one workgroup per (batch*head, key tile), W waves of 32
-//                    keys, K and V in registers; Q, dO, L2 and D tiles of the
-//                    query tiles that can see its keys stream through an LDS ring.
+//                    keys, K and V in registers; Q, dO, L2 and -D tiles of the
+//                    query tiles that can see its keys stream through an LDS ring
+//                    (d = 64: bwd_dkdv_pipe_kernel, the same work software-
+//                    pipelined over 32-query tiles).
+// Both passes start the dP accumulators from -D, so that the products leave
+// dP - D and dS = P (dP - D) takes one multiply.
 // Both rings are filled with global_load_lds_dwordx4 into row-major,
 // chunk-swizzled tiles (see fa_device.h); a ring of 2*GR slots takes one
 // barrier per GR tiles (GR tiles computed on while the next GR are in flight).
@@ -225,10 +229,17 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    sacc[qb][kb][r] = 0.f;
-                    pacc[qb][kb][r] = 0.f;
-                }
+                for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
+            // dP starts from -D of its queries, so that the products leave
+            // dP - D (register r: query 8*(r/4) + 4g + r%4 of the block)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4 nd = *(const f32x4 *)(dt + qb * 32 + 8 * r4 + 4 * g);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pacc[qb][kb][4 * r4 + e] = nd[e];
+            }
 #pragma unroll
             for (int ds = 0; ds < D / 16; ++ds) {
                 const int off = qb * 32 * ROWB + roff[ds];
@@ -264,7 +275,6 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int qi = qb * 32 + 8 * r4 + 4 * g;
                 const f32x4 lv = *(const f32x4 *)(lt + qi);
-                const f32x4 dv = *(const f32x4 *)(dt + qi);
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -273,7 +283,7 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
                         float p = fast_exp2(fmaf(sacc[qb][kb][r], c, -lv[e]));
                         if (MASKED && (qi + e < lo[kb] || qi + e > hi[kb])) p = 0.f;
                         sacc[qb][kb][r] = p;
-                        pacc[qb][kb][r] = p * (pacc[qb][kb][r] - dv[e]);
+                        pacc[qb][kb][r] = p * pacc[qb][kb][r];
                     }
             }
         };
@@ -382,6 +392,287 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV: key-major and software-pipelined over 32-query tiles (d = 64).
+// ---------------------------------------------------------------------------
+// Each wave owns 32 keys (K and V in registers) and walks the query tiles that
+// see them; step t forms S and dP of tile t+1 on the matrix cores while its
+// vector work turns tile t's S and dP into P and dS, then accumulates dV and
+// dK with tile t.  The two sets of tiles alternate between register sets, so
+// every stretch of the step has both matrix and vector work in the same wave.
+// The eight waves of a workgroup share one LDS ring of Q, dO, L2 and -D tiles:
+// a ring of 2*GR + 1 slots with one barrier per GR tiles (the barrier
+// publishes tiles t+1 .. t+GR and frees the slots of t-GR .. t-1).
+template <int D, int GR_, int W_>
+struct DkdvPipeCfg {
+    static constexpr int W = W_;                   // waves per workgroup
+    static constexpr int BR = 32;                  // queries per tile
+    static constexpr int KEYS = 32 * W;            // keys per workgroup
+    static constexpr int CH = D / 8, ROWB = D * 2;
+    static constexpr int TILEB = BR * ROWB;        // one Q or dO tile
+    static constexpr int NB = TILEB / 1024;        // 1 KiB blocks per tile
+    static constexpr int RPI = 1024 / ROWB;        // rows per 1 KiB block
+    static constexpr int VECB = 256;               // one L2 or -D slice (64 lanes x 4 B)
+    static constexpr int STAGEB = 2 * TILEB + 2 * VECB;
+    static constexpr int GR = GR_;                 // query tiles per LDS barrier
+    static constexpr int ST = 2 * GR + 1;          // ring slots
+    static_assert(2 * NB == W, "one 1 KiB load per wave per tile");
+    static_assert(GR >= 1 && ST * STAGEB <= 160 * 1024, "ring fits the 160 KiB LDS");
+};
+
+template <int D, int GR, int W, bool CAUSAL>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+                          const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
+                          const float *__restrict__ L2, const float *__restrict__ Dv,
+                          uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int64_t Nq,
+                          int64_t Nk, int64_t qoff, int nkt, uint32_t group, float scale, float c) {
+    using T = DkdvPipeCfg<D, GR, W>;
+    constexpr int ST = T::ST, ROWB = T::ROWB, BR = T::BR;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * T::STAGEB];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int g = lane >> 5, lr = lane & 31;
+    const uint32_t wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const TileId tid_ = tile_order(blockIdx.x, gridDim.x / (uint32_t)nkt, (uint32_t)nkt, group);
+    const int64_t bh = tid_.head;
+    const int64_t k0 = (int64_t)tid_.rank * T::KEYS;  // causal: early keys are seen by the most queries
+    const int64_t kw0 = k0 + 32 * (int64_t)wave_u;     // this wave's keys: kw0 + lane%32
+    const uint16_t *Qh = Q + bh * Nq * D;
+    const uint16_t *dOh = dO + bh * Nq * D;
+    const float *L2h = L2 + bh * Nq;
+    const float *Dh = Dv + bh * Nq;
+
+    // K and V of this wave's keys: B operands of S = Q K^T and dP = dO V^T
+    bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+        kf[ds] = __builtin_bit_cast(bf16x8, load_row16(K + bh * Nk * D, kw0 + lr, Nk, D, ds * 2 + g));
+        vf[ds] = __builtin_bit_cast(bf16x8, load_row16(V + bh * Nk * D, kw0 + lr, Nk, D, ds * 2 + g));
+    }
+
+    // ---- ring loads: load j of a tile (one per wave) fills 1 KiB block j of
+    //      the stage (Q blocks, then dO blocks); this lane writes chunk `lane`
+    //      of the block, i.e. row (j % NB)*RPI + lane/CH of its tile with
+    //      logical chunk (lane % CH) ^ swz(row).  Loads 0 and 1 also fill the
+    //      L2 and -D slices.  With FA_BWD_DMA_ALT, wave w also issues the load
+    //      of its partner w ^ 4, one barrier in two.
+    constexpr bool ALT = FA_BWD_DMA_ALT && W == 8;
+    const uint32_t owner_u[2] = {wave_u, wave_u ^ 4u};
+    uint32_t ld_off[2];
+#pragma unroll
+    for (int o = 0; o < 2; ++o)
+        ld_off[o] = (uint32_t)chunk_off<ROWB>((int)(owner_u[o] % T::NB) * T::RPI + lane / T::CH,
+                                              lane % T::CH);
+    auto issue_as = [&](int it, int st, int o) __attribute__((always_inline)) {
+        const uint32_t j = owner_u[o];
+        const int64_t q0 = (int64_t)it * BR;
+        const uint32_t sb = lds_addr(smem) + st * T::STAGEB;
+        const uint16_t *src = j < (uint32_t)T::NB ? Qh : dOh;
+        const uint32_t vb = sb + 2 * T::TILEB + j * T::VECB;  // j = 0: L2, j = 1: -D
+        if (q0 + 64 <= Nq) {  // every row and vector lane below in range: scalar base
+            dma16_s(src + q0 * D, ld_off[o], sb + j * 1024);
+            if (j < 2) dma4((j == 0 ? L2h : Dh) + q0 + lane, vb);
+            return;
+        }
+        const int row = (int)(j % T::NB) * T::RPI + lane / T::CH;
+        const int64_t q = q0 + row < Nq ? q0 + row : Nq - 1;  // past the end: masked later
+        dma16((const uint8_t *)(src + q * D) + (ld_off[o] - row * ROWB), sb + j * 1024);
+        if (j < 2) {
+            int64_t qv = q0 + lane;
+            qv = qv < Nq ? qv : Nq - 1;
+            dma4((j == 0 ? L2h : Dh) + qv, vb);
+        }
+    };
+
+    int roff[D / 16], toff[D / 32];
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) roff[ds] = chunk_off<ROWB>(lr, 2 * ds + g);
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) toff[b] = tr_off<ROWB>(lane, b, 0);
+
+    f32x16 dvacc[D / 32], dkacc[D / 32];
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            dvacc[b][r] = 0.f;
+            dkacc[b][r] = 0.f;
+        }
+
+    // S = Q K^T and dP - D = dO V^T - D of the tile in slot st (lane: key lr;
+    // register r: query 8*(r/4) + 4g + r%4 of the tile)
+    auto sdp = [&](int st, f32x16 &sa, f32x16 &pa) __attribute__((always_inline)) {
+        const uint8_t *qt = smem + st * T::STAGEB;
+        const uint8_t *ot = qt + T::TILEB;
+        const float *dt = (const float *)(ot + T::TILEB) + T::VECB / 4;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sa[r] = 0.f;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 nd = *(const f32x4 *)(dt + 8 * r4 + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pa[4 * r4 + e] = nd[e];
+        }
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) {
+            const bf16x8 aq = *(const bf16x8 *)(qt + roff[ds]);
+            const bf16x8 ao = *(const bf16x8 *)(ot + roff[ds]);
+            sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ds], sa, 0, 0, 0);
+            pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[ds], pa, 0, 0, 0);
+        }
+    };
+    // P = exp2(S c - L2), dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS
+    // with the tile in slot st (query offset o of the tile is visible to this
+    // lane's key iff lo <= o <= hi; MASKED instances only)
+    auto finish = [&](int st, int64_t q0, f32x16 &sa, f32x16 &pa, auto masked) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked)::value;
+        const uint8_t *qt = smem + st * T::STAGEB;
+        const uint8_t *ot = qt + T::TILEB;
+        const float *lt = (const float *)(ot + T::TILEB);
+        int lo = 0, hi = BR - 1;
+        if (MASKED) {
+            const int64_t key = kw0 + lr;
+            int64_t lo64 = CAUSAL ? key - qoff - q0 : 0;
+            int64_t hi64 = Nq - 1 - q0;
+            if (key >= Nk) hi64 = -1;
+            lo = (int)(lo64 < 0 ? 0 : (lo64 > BR ? BR : lo64));
+            hi = (int)(hi64 > BR - 1 ? BR - 1 : (hi64 < -1 ? -1 : hi64));
+        }
+        // k-step kq of the products takes queries 16kq .. 16kq+15: registers
+        // 8kq .. 8kq+7 (k-slot (g, e) is query 8*(e/4) + 4g + e%4 of the step),
+        // and the transposed operands are read in the same slot order
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) {
+#pragma unroll
+            for (int r4 = 2 * kq; r4 < 2 * kq + 2; ++r4) {
+                const int qi = 8 * r4 + 4 * g;
+                const f32x4 lv = *(const f32x4 *)(lt + qi);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * r4 + e;
+                    float p = fast_exp2(fmaf(sa[r], c, -lv[e]));
+                    if (MASKED && (qi + e < lo || qi + e > hi)) p = 0.f;
+                    sa[r] = p;
+                    pa[r] = p * pa[r];
+                }
+            }
+            const bf16x8 pb = pack8(sa, 8 * kq), sb = pack8(pa, 8 * kq);
+#pragma unroll
+            for (int b = 0; b < D / 32; ++b) {
+                const bf16x8 ao = tr_pair<ROWB>(ot + kq * 16 * ROWB, toff[b]);
+                const bf16x8 aq = tr_pair<ROWB>(qt + kq * 16 * ROWB, toff[b]);
+                dvacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb, dvacc[b], 0, 0, 0);
+                dkacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb, dkacc[b], 0, 0, 0);
+            }
+        }
+    };
+
+    // query tiles that see this workgroup's keys (causal: query q sees keys
+    // 0 .. q + qoff) and the ones that see this wave's: from its on; tiles
+    // before ifull cross the causal diagonal, tiles from pend on are ragged
+    const int nqt = (int)((Nq + BR - 1) / BR);
+    const int it0 = CAUSAL ? (int)(k0 - qoff > 0 ? (k0 - qoff) / BR : 0) : 0;
+    int its = it0, ifull = it0;
+    if (CAUSAL) {
+        const int64_t a = kw0 - qoff - (BR - 1);  // first query tile whose last query sees kw0
+        if (a > 0 && (a + BR - 1) / BR > its) its = (int)((a + BR - 1) / BR);
+        const int64_t f = kw0 + 31 - qoff;        // first tile whose first query sees every key
+        ifull = f > 0 ? (int)((f + BR - 1) / BR) : 0;
+        if (ifull < its) ifull = its;
+    }
+    if (kw0 >= Nk) its = ifull = nqt;     // no keys: ring steps only
+    if (kw0 + 32 > Nk) ifull = nqt;        // ragged keys: every tile is masked
+    const int pend = (int)(Nq / BR);       // tiles before pend have no ragged queries
+
+    auto ring = [&](int idx) __attribute__((always_inline)) {
+        if (idx % GR != 0) return;
+        wait_vm<0>();
+        lds_barrier();
+        if (ALT && ((idx / GR) & 1) != (int)(wave_u >> 2)) return;
+#pragma unroll
+        for (int t = GR + 1; t <= 2 * GR; ++t)
+            if (it0 + idx + t < nqt) {
+                issue_as(it0 + idx + t, (idx + t) % ST, 0);
+                if (ALT) issue_as(it0 + idx + t, (idx + t) % ST, 1);
+            }
+    };
+
+#if FA_STATS
+    uint32_t st_tiles = 0;
+#endif
+    f32x16 s0, p0, s1, p1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s0[r] = p0[r] = s1[r] = p1[r] = 0.f;
+#pragma unroll
+    for (int t = 0; t <= GR; ++t)
+        if (it0 + t < nqt) issue_as(it0 + t, t, 0);
+    wait_vm<0>();
+    lds_barrier();
+    if (it0 < nqt && its == it0) sdp(0, s0, p0);
+
+    const std::integral_constant<bool, false> plain;
+    const std::integral_constant<bool, true> generic;
+    // one step with the tile of step it in (s0, p0) on entry and that of it+1
+    // in (s0, p0) on exit; the mask is decided per tile
+    auto gstep = [&](int it) __attribute__((always_inline)) {
+        const int idx = it - it0;
+        ring(idx);
+        if (it + 1 < nqt && it + 1 >= its) sdp((idx + 1) % ST, s1, p1);
+        if (it >= its) {
+#if FA_STATS
+            ++st_tiles;
+#endif
+            const int64_t q0 = (int64_t)it * BR;
+            if (it < ifull || it >= pend)
+                finish(idx % ST, q0, s0, p0, generic);
+            else
+                finish(idx % ST, q0, s0, p0, plain);
+        }
+        s0 = s1;
+        p0 = p1;
+    };
+    int it = it0;
+    for (; it < nqt && it < ifull; ++it) gstep(it);
+    for (; it + 2 < nqt && it + 1 < pend; it += 2) {  // tiles it, it+1 unmasked; sets alternate
+        const int idx = it - it0;
+#if FA_STATS
+        st_tiles += 2;
+#endif
+        ring(idx);
+        sdp((idx + 1) % ST, s1, p1);
+        finish(idx % ST, (int64_t)it * BR, s0, p0, plain);
+        ring(idx + 1);
+        sdp((idx + 2) % ST, s0, p0);
+        finish((idx + 1) % ST, (int64_t)(it + 1) * BR, s1, p1, plain);
+    }
+    for (; it < nqt; ++it) gstep(it);
+
+#if FA_STATS
+    if (lane == 0 && kw0 < Nk) atomicAdd(&g_bwd_stats[3], (unsigned long long)st_tiles);
+#endif
+    // ---- epilogue: dK = scale * dK_acc, dV = dV_acc (lane: key lr; register
+    //      r: column 32b + 8*(r/4) + 4g + r%4)
+    const int64_t key = kw0 + lr;
+    if (key < Nk) {
+        uint16_t *dKr = dK + (bh * Nk + key) * D;
+        uint16_t *dVr = dV + (bh * Nk + key) * D;
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int col = b * 32 + 8 * t + 4 * g;
+                const f32x16 &ka = dkacc[b], &va = dvacc[b];
+                const u32x2 wk = {pack_bf16x2(scale * ka[4 * t], scale * ka[4 * t + 1]),
+                                  pack_bf16x2(scale * ka[4 * t + 2], scale * ka[4 * t + 3])};
+                const u32x2 wv = {pack_bf16x2(va[4 * t], va[4 * t + 1]),
+                                  pack_bf16x2(va[4 * t + 2], va[4 * t + 3])};
+                *(u32x2 *)(dKr + col) = wk;
+                *(u32x2 *)(dVr + col) = wv;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // dQ: query-major.
 // ---------------------------------------------------------------------------
 #ifndef FA_BWD_DQ_WPE  // waves per SIMD of the dQ pass
@@ -441,7 +732,8 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     // S^T = K Q^T and dP^T = V dO^T; each K and V fragment read from LDS
     // serves the QB blocks
     bf16x8 qf[QB][D / 16], of[QB][D / 16];
-    float l2[QB], dq[QB];
+    float l2[QB];
+    f32x16 nd[QB];  // -D of this lane's query in every register: dP^T starts from it
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int64_t qrow = qw0 + 32 * qb + lr;
@@ -469,10 +761,11 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
         const float lrow = L[bh * Nq + qc];
         if (g == 0 && qrow < Nq) {
             L2[bh * Nq + qc] = lrow * kLog2e;
-            Dv[bh * Nq + qc] = dsum;
+            Dv[bh * Nq + qc] = -dsum;
         }
         l2[qb] = qrow < Nq ? lrow * kLog2e : INFINITY;  // padded row: P = 0
-        dq[qb] = qrow < Nq ? dsum : 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) nd[qb][r] = qrow < Nq ? -dsum : 0.f;
     }
 
     constexpr bool ALT = FA_BWD_DMA_ALT && W == 8 && GR > 1;
@@ -547,12 +840,11 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
             //      register r: key 8*(r/4) + 4g + r%4 of the 32-key block)
             f32x16 sacc[QB], pacc[QB];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
+            for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    sacc[qb][r] = 0.f;
-                    pacc[qb][r] = 0.f;
-                }
+                for (int r = 0; r < 16; ++r) sacc[qb][r] = 0.f;
+                pacc[qb] = nd[qb];  // the products leave dP^T - D
+            }
 #pragma unroll
             for (int ds = 0; ds < D / 16; ++ds) {
                 const int off = kb * 32 * ROWB + koff[ds];
@@ -580,7 +872,7 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
                 for (int r = 0; r < 16; ++r) {
                     float p = fast_exp2(fmaf(sacc[qb][r], c, -l2[qb]));
                     if (MASKED && 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
-                    pacc[qb][r] = p * (pacc[qb][r] - dq[qb]);
+                    pacc[qb][r] = p * pacc[qb][r];
                 }
             }
             // ---- dQ^T += K^T dS^T.  B operand (k-step h of 16 keys) = registers
@@ -702,6 +994,12 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 #ifndef FA_BWD_DKDV_KB64  // 32-key blocks per wave in the dK/dV pass, d = 64
 #define FA_BWD_DKDV_KB64 1
 #endif
+#ifndef FA_BWD_DKDV_PIPE  // 1: d = 64 runs the software-pipelined dK/dV pass
+#define FA_BWD_DKDV_PIPE 1
+#endif
+#ifndef FA_BWD_GR_PIPE  // its query tiles per LDS barrier
+#define FA_BWD_GR_PIPE 8
+#endif
 
 template <int D, bool CAUSAL>
 struct DkdvChoice {
@@ -733,7 +1031,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_main(const BwdArgs &a, hipStream_t s) {
     using C = DkdvChoice<D, CAUSAL>;
     using QC = DqChoice<D>;
-    // the dQ pass first: it also writes D and L2, which the dK/dV pass reads
+    // the dQ pass first: it also writes -D and L2, which the dK/dV pass reads
     const int nqt = (int)((a.Nq + QC::Cfg::BR - 1) / QC::Cfg::BR);
     hipLaunchKernelGGL((bwd_dq_kernel<D, QC::BC, QC::GR, QC::W, QC::QB, CAUSAL>),
                        dim3((unsigned)(a.B * a.H * nqt)), dim3(QC::W * 64), 0, s,
@@ -743,13 +1041,24 @@ hipError_t launch_main(const BwdArgs &a, hipStream_t s) {
                        a.scale, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int nkt = (int)((a.Nk + C::Cfg::KEYS - 1) / C::Cfg::KEYS);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, C::BR, C::GR, C::KB, C::W, CAUSAL>),
-                       dim3((unsigned)(a.B * a.H * nkt)), dim3(C::W * 64), 0, s,
-                       (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
-                       (const uint16_t *)a.dO, a.L2, a.D, (uint16_t *)a.dK, (uint16_t *)a.dV,
-                       a.Nq, a.Nk, a.q_start, nkt, tile_group(a.B * a.H), a.scale,
-                       a.scale * kLog2e);
+    if constexpr (D == 64 && FA_BWD_DKDV_PIPE) {
+        using P = DkdvPipeCfg<D, FA_BWD_GR_PIPE, 8>;
+        const int nkt = (int)((a.Nk + P::KEYS - 1) / P::KEYS);
+        hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<D, FA_BWD_GR_PIPE, 8, CAUSAL>),
+                           dim3((unsigned)(a.B * a.H * nkt)), dim3(8 * 64), 0, s,
+                           (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
+                           (const uint16_t *)a.dO, a.L2, a.D, (uint16_t *)a.dK, (uint16_t *)a.dV,
+                           a.Nq, a.Nk, a.q_start, nkt, tile_group(a.B * a.H), a.scale,
+                           a.scale * kLog2e);
+    } else {
+        const int nkt = (int)((a.Nk + C::Cfg::KEYS - 1) / C::Cfg::KEYS);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, C::BR, C::GR, C::KB, C::W, CAUSAL>),
+                           dim3((unsigned)(a.B * a.H * nkt)), dim3(C::W * 64), 0, s,
+                           (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
+                           (const uint16_t *)a.dO, a.L2, a.D, (uint16_t *)a.dK, (uint16_t *)a.dV,
+                           a.Nq, a.Nk, a.q_start, nkt, tile_group(a.B * a.H), a.scale,
+                           a.scale * kLog2e);
+    }
     return hipGetLastError();
 }
 
@@ -768,6 +1077,7 @@ void bwd_bf16_tiles(int64_t d, int causal, int64_t *kv_rows, int64_t *kv_cols, i
                     int64_t *q_cols) {
     *kv_rows = d == 64 ? (causal ? 32 * DkdvChoice<64, true>::KB : 32 * DkdvChoice<64, false>::KB) : 32;
     *kv_cols = d == 64 ? (causal ? DkdvChoice<64, true>::BR : DkdvChoice<64, false>::BR) : 32;
+    if (d == 64 && FA_BWD_DKDV_PIPE) *kv_rows = *kv_cols = 32;
     *q_rows = d == 64 ? 32 * FA_BWD_DQ_QB64 : 32;
     *q_cols = d == 64 ? FA_BWD_DQ_BC64 : 32;
 }

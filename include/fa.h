@@ -111,8 +111,8 @@ fa_status fa_fwd_blocked(fa_dtype dt, const void *Q, const void *K, const void *
 
 /*
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs: the row
- * sums D = rowsum(dO * O) and L * log2(e), each [B][H][Nq] fp32 rounded up to
- * 256 bytes.  Returns 0 for invalid sizes.
+ * sums D = rowsum(dO * O) (the bf16 kernels store -D) and L * log2(e), each
+ * [B][H][Nq] fp32 rounded up to 256 bytes.  Returns 0 for invalid sizes.
  */
 size_t fa_bwd_workspace_size(fa_dtype dt, int64_t B, int64_t H, int64_t Nq, int64_t d);
 
