@@ -49,6 +49,11 @@
 #ifndef FA_BWD_DMA_ALT
 #define FA_BWD_DMA_ALT 1
 #endif
+// with FA_BWD_DMA_ALT: wave priority of the loading wave until the next
+// barrier (s_setprio), so that it catches up with its partner (1.5 %)
+#ifndef FA_BWD_PRIO
+#define FA_BWD_PRIO 1
+#endif
 
 namespace fa {
 namespace {
@@ -588,6 +593,7 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
         if (idx % GR != 0) return;
         wait_vm<0>();
         lds_barrier();
+        if (ALT && FA_BWD_PRIO) __builtin_amdgcn_s_setprio(0);
         if (ALT && ((idx / GR) & 1) != (int)(wave_u >> 2)) return;
 #pragma unroll
         for (int t = GR + 1; t <= 2 * GR; ++t)
@@ -595,6 +601,8 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
                 issue_as(it0 + idx + t, (idx + t) % ST, 0);
                 if (ALT) issue_as(it0 + idx + t, (idx + t) % ST, 1);
             }
+        // the loading wave is behind its partner: let it catch up
+        if (ALT && FA_BWD_PRIO) __builtin_amdgcn_s_setprio(FA_BWD_PRIO);
     };
 
 #if FA_STATS
@@ -901,6 +909,7 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
         if (j % GR != 0) return;  // one barrier per GR tiles, as in the dK/dV pass
         wait_vm<0>();
         lds_barrier();
+        if (ALT && FA_BWD_PRIO) __builtin_amdgcn_s_setprio(0);
         if (ALT && ((j / GR) & 1) != (wave >> 2)) return;
 #pragma unroll
         for (int t = GR; t < 2 * GR; ++t)
@@ -908,6 +917,8 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
                 issue_as(j + t, (int)((j + t) % ST), 0);
                 if (ALT) issue_as(j + t, (int)((j + t) % ST), 1);
             }
+        // the loading wave is behind its partner: let it catch up
+        if (ALT && FA_BWD_PRIO) __builtin_amdgcn_s_setprio(FA_BWD_PRIO);
     };
     // leading tiles with every key visible to every query of this wave
     int64_t nfull = 0;

@@ -86,6 +86,12 @@
 #ifndef FA_FWD_DMA_ALT
 #define FA_FWD_DMA_ALT 1
 #endif
+// with FA_FWD_DMA_ALT: wave priority of the loading wave until the next
+// barrier (s_setprio), so that it catches up with its partner: 1.5 % faster
+// at causal d = 128, level at d = 64
+#ifndef FA_FWD_PRIO
+#define FA_FWD_PRIO 1
+#endif
 
 namespace fa {
 namespace {
@@ -467,6 +473,7 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
             if constexpr (ALT) {
                 // one wave of each SIMD's pair loads for both, in turn: its
                 // partner computes meanwhile instead of queueing for the loads
+                if (FA_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
                 if (((t / GR) & 1) != (wave >> 2)) return;
 #pragma unroll
                 for (int j = GR + 1; j <= 2 * GR; ++j)
@@ -474,6 +481,8 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
                         issue_as(t + j, (t + j) % S, 0);
                         issue_as(t + j, (t + j) % S, 1);
                     }
+                // the loading wave is behind its partner: let it catch up
+                if (FA_FWD_PRIO) __builtin_amdgcn_s_setprio(FA_FWD_PRIO);
                 return;
             }
 #pragma unroll
