@@ -527,9 +527,11 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
         }
     };
     // P = exp2(S c - L2), dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS
-    // with the tile in slot st (query offset o of the tile is visible to this
-    // lane's key iff lo <= o <= hi; MASKED instances only)
-    auto finish = [&](int st, int64_t q0, f32x16 &sa, f32x16 &pa, auto masked) __attribute__((always_inline)) {
+    // with the tile in slot st.  MASKED instances: query offset 8*(r/4) + 4g +
+    // r%4 of register r is visible to this lane's key iff lo <= 8*(r/4) + r%4
+    // <= hi (lo and hi less 4g, so that the offsets compared are constants)
+    auto finish = [&](int st, int64_t q0, f32x16 &sa, f32x16 &pa, auto masked)
+                      __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked)::value;
         const uint8_t *qt = smem + st * T::STAGEB;
         const uint8_t *ot = qt + T::TILEB;
@@ -540,8 +542,8 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
             int64_t lo64 = CAUSAL ? key - qoff - q0 : 0;
             int64_t hi64 = Nq - 1 - q0;
             if (key >= Nk) hi64 = -1;
-            lo = (int)(lo64 < 0 ? 0 : (lo64 > BR ? BR : lo64));
-            hi = (int)(hi64 > BR - 1 ? BR - 1 : (hi64 < -1 ? -1 : hi64));
+            lo = (int)(lo64 < 0 ? 0 : (lo64 > BR ? BR : lo64)) - 4 * g;
+            hi = (int)(hi64 > BR - 1 ? BR - 1 : (hi64 < -1 ? -1 : hi64)) - 4 * g;
         }
         // k-step kq of the products takes queries 16kq .. 16kq+15: registers
         // 8kq .. 8kq+7 (k-slot (g, e) is query 8*(e/4) + 4g + e%4 of the step),
@@ -550,13 +552,12 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
         for (int kq = 0; kq < 2; ++kq) {
 #pragma unroll
             for (int r4 = 2 * kq; r4 < 2 * kq + 2; ++r4) {
-                const int qi = 8 * r4 + 4 * g;
-                const f32x4 lv = *(const f32x4 *)(lt + qi);
+                const f32x4 lv = *(const f32x4 *)(lt + 8 * r4 + 4 * g);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * r4 + e;
                     float p = fast_exp2(fmaf(sa[r], c, -lv[e]));
-                    if (MASKED && (qi + e < lo || qi + e > hi)) p = 0.f;
+                    if (MASKED && (8 * r4 + e < lo || 8 * r4 + e > hi)) p = 0.f;
                     sa[r] = p;
                     pa[r] = p * pa[r];
                 }
@@ -610,37 +611,34 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
 #endif
     f32x16 s0, p0, s1, p1;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s0[r] = p0[r] = s1[r] = p1[r] = 0.f;
-#pragma unroll
     for (int t = 0; t <= GR; ++t)
         if (it0 + t < nqt) issue_as(it0 + t, t, 0);
     wait_vm<0>();
     lds_barrier();
-    if (it0 < nqt && its == it0) sdp(0, s0, p0);
 
     const std::integral_constant<bool, false> plain;
     const std::integral_constant<bool, true> generic;
-    // one step with the tile of step it in (s0, p0) on entry and that of it+1
-    // in (s0, p0) on exit; the mask is decided per tile
+    // a step without pipelining, for the tiles on the causal diagonal, the
+    // ragged ends and the steps before this wave's first tile
     auto gstep = [&](int it) __attribute__((always_inline)) {
         const int idx = it - it0;
         ring(idx);
-        if (it + 1 < nqt && it + 1 >= its) sdp((idx + 1) % ST, s1, p1);
-        if (it >= its) {
+        if (it < its) return;
 #if FA_STATS
-            ++st_tiles;
+        ++st_tiles;
 #endif
-            const int64_t q0 = (int64_t)it * BR;
-            if (it < ifull || it >= pend)
-                finish(idx % ST, q0, s0, p0, generic);
-            else
-                finish(idx % ST, q0, s0, p0, plain);
-        }
-        s0 = s1;
-        p0 = p1;
+        sdp(idx % ST, s0, p0);
+        const int64_t q0 = (int64_t)it * BR;
+        if (it < ifull || it >= pend)
+            finish(idx % ST, q0, s0, p0, generic);
+        else
+            finish(idx % ST, q0, s0, p0, plain);
     };
     int it = it0;
     for (; it < nqt && it < ifull; ++it) gstep(it);
+    // pipelined steps over unmasked tiles (tile it is visible here: published
+    // by the last barrier, or by the one before the loop)
+    if (it + 2 < nqt && it + 1 < pend) sdp((it - it0) % ST, s0, p0);
     for (; it + 2 < nqt && it + 1 < pend; it += 2) {  // tiles it, it+1 unmasked; sets alternate
         const int idx = it - it0;
 #if FA_STATS
