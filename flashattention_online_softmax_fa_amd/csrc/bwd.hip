@@ -442,10 +442,10 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
     const int64_t bh = tid_.head;
     const int64_t k0 = (int64_t)tid_.rank * T::KEYS;  // causal: early keys are seen by the most queries
     const int64_t kw0 = k0 + 32 * (int64_t)wave_u;     // this wave's keys: kw0 + lane%32
-    const uint16_t *Qh = Q + bh * Nq * D;
-    const uint16_t *dOh = dO + bh * Nq * D;
-    const float *L2h = L2 + bh * Nq;
-    const float *Dh = Dv + bh * Nq;
+    const uint16_t *Qh = uniform_ptr(Q + bh * Nq * D);
+    const uint16_t *dOh = uniform_ptr(dO + bh * Nq * D);
+    const float *L2h = uniform_ptr(L2 + bh * Nq);
+    const float *Dh = uniform_ptr(Dv + bh * Nq);
 
     // K and V of this wave's keys: B operands of S = Q K^T and dP = dO V^T
     bf16x8 kf[D / 16], vf[D / 16];
@@ -468,25 +468,25 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
     for (int o = 0; o < 2; ++o)
         ld_off[o] = (uint32_t)chunk_off<ROWB>((int)(owner_u[o] % T::NB) * T::RPI + lane / T::CH,
                                               lane % T::CH);
+    // (scalar bases at the tile and 32-bit lane offsets; rows and vector
+    // lanes past Nq re-read row Nq-1, masked later)
     auto issue_as = [&](int it, int st, int o) __attribute__((always_inline)) {
         const uint32_t j = owner_u[o];
         const int64_t q0 = (int64_t)it * BR;
         const uint32_t sb = lds_addr(smem) + st * T::STAGEB;
-        const uint16_t *src = j < (uint32_t)T::NB ? Qh : dOh;
+        const uint16_t *src = (j < (uint32_t)T::NB ? Qh : dOh) + q0 * D;
         const uint32_t vb = sb + 2 * T::TILEB + j * T::VECB;  // j = 0: L2, j = 1: -D
-        if (q0 + 64 <= Nq) {  // every row and vector lane below in range: scalar base
-            dma16_s(src + q0 * D, ld_off[o], sb + j * 1024);
-            if (j < 2) dma4((j == 0 ? L2h : Dh) + q0 + lane, vb);
+        const float *vsrc = (j == 0 ? L2h : Dh) + q0;
+        if (q0 + 64 <= Nq) {  // every row and vector lane below in range
+            dma16_s(src, ld_off[o], sb + j * 1024);
+            if (j < 2) dma4_s(vsrc, 4u * (uint32_t)lane, vb);
             return;
         }
+        const int last = (int)(Nq - 1 - q0);  // last row of the tile in range
         const int row = (int)(j % T::NB) * T::RPI + lane / T::CH;
-        const int64_t q = q0 + row < Nq ? q0 + row : Nq - 1;  // past the end: masked later
-        dma16((const uint8_t *)(src + q * D) + (ld_off[o] - row * ROWB), sb + j * 1024);
-        if (j < 2) {
-            int64_t qv = q0 + lane;
-            qv = qv < Nq ? qv : Nq - 1;
-            dma4((j == 0 ? L2h : Dh) + qv, vb);
-        }
+        const int rr = row < last ? row : last;
+        dma16_s(src, ld_off[o] + (uint32_t)((rr - row) * ROWB), sb + j * 1024);
+        if (j < 2) dma4_s(vsrc, 4u * (uint32_t)(lane < last ? lane : last), vb);
     };
 
     int roff[D / 16], toff[D / 32];

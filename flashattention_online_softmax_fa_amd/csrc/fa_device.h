@@ -169,6 +169,28 @@ __device__ __forceinline__ void dma16_s(const void *base, uint32_t off, uint8_t 
     dma16_s(base, off, lds_addr(dst));
 }
 
+// A wave-uniform pointer moved to scalar registers (read from the first lane),
+// so that values derived from it stay on the scalar unit.
+template <typename T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    return (T *)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
+// 4-byte DMA with a wave-uniform base and a 32-bit per-lane byte offset:
+// lane i of the wave writes lds + 4*i.
+__device__ __forceinline__ void dma4_s(const void *base, uint32_t off, uint32_t lds) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint64_t u = ((uint64_t)hi << 32) | (uint64_t)lo;
+    __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                     :: "v"(off), "s"((const void *)(uintptr_t)u),
+                        "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+
 // 4-byte DMA: lane i of the wave writes lds + 4*i.
 __device__ __forceinline__ void dma4(const void *src, uint32_t lds) {
     __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
