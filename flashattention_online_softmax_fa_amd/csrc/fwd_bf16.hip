@@ -52,6 +52,7 @@
 // FMA; L is converted back to the natural logarithm at the end.
 #include "fa_device.h"
 #include "fa_internal.h"
+#include "fwd128_step.inc"
 
 #include <type_traits>
 
@@ -98,6 +99,13 @@
 #endif
 #ifndef FA_FWD_IGLP128
 #define FA_FWD_IGLP128 2
+#endif
+// 1: the mask-free steps of the d = 128 forward (one 32-query block per wave,
+// 32-key tiles, 8 ring slots) run the generated assembly of fwd128_step.inc,
+// with its own instruction order (0.5 % faster than the compiler's step at
+// causal d = 128, where the LDS read rate sets the pace)
+#ifndef FA_FWD_ASM128
+#define FA_FWD_ASM128 1
 #endif
 #ifndef FA_FWD_PRIO
 #define FA_FWD_PRIO 1
@@ -153,6 +161,8 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     using T = Tile<D, QB, BC, ST, W, GR>;
     constexpr int S = T::STAGES;
     constexpr int KB = BC / 32;  // 32-key blocks per tile
+    // the generated mask-free step (fwd128_step.inc) for this configuration
+    constexpr bool ASM = FA_FWD_ASM128 && D == 128 && QB == 1 && BC == 32 && S == 8 && W == 8 && POS_SCALE;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[S * 2 * T::TILEB];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -214,7 +224,9 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
             const int j = ow * T::LPW + u;  // wave-uniform
             const bool is_v = j >= T::NB;
             const uint8_t *src = is_v ? vt : kt;
-            uint8_t *dst = smem + st * 2 * T::TILEB + j * 1024;  // V follows K in the slot
+            // V follows K in the slot (ASM: K tiles of all slots, then V tiles)
+            uint8_t *dst = ASM ? smem + (is_v ? S * T::TILEB + (j - T::NB) * 1024 : j * 1024) + st * T::TILEB
+                               : smem + st * 2 * T::TILEB + j * 1024;
             if (full) {
                 dma16_s(src, (uint32_t)ld_off[owner][u], dst);
             } else {  // rows past Nk re-read the last key; they are masked
@@ -228,19 +240,40 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     // wait until at most n ring steps of this wave's loads are still in flight
     auto wait_pending = [&](int n) { wait_steps<T::LPW, S - 2>(n); };
 
-    // ---- per-lane constants of the LDS reads
+    // ---- per-lane constants of the LDS reads (byte offsets within a tile;
+    //      with the generated d = 128 step, LDS addresses, which it takes in
+    //      fixed registers)
+    const int lbase = ASM ? (int)lds_addr(smem) : 0;
     // K (A operand of S^T): row kb*32 + lr, logical chunk 2*ds + g
     int koff[D / 16];
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) koff[ds] = chunk_off<T::ROWB>(lr, 2 * ds + g);
+    for (int ds = 0; ds < D / 16; ++ds) koff[ds] = lbase + chunk_off<T::ROWB>(lr, 2 * ds + g);
     // V^T (A operand of O^T, transposed read): rows 16ks + 8h + 4g + (lane%16)/4,
     // columns 32b + 16*((lane/16)%2) + 4*(lane%4)
     int voff[D / 32][2];
 #pragma unroll
     for (int b = 0; b < D / 32; ++b) {
-        voff[b][0] = tr_off<T::ROWB>(lane, b, 0);
-        voff[b][1] = tr_off<T::ROWB>(lane, b, 1);
+        voff[b][0] = lbase + tr_off<T::ROWB>(lane, b, 0);
+        voff[b][1] = lbase + tr_off<T::ROWB>(lane, b, 1);
+        if constexpr (ASM) {  // the V tiles start S * TILEB up
+            voff[b][0] += S * T::TILEB;
+            voff[b][1] += S * T::TILEB;
+        }
     }
+    // Where the K and V tiles of ring slot st start: K then V in each slot, or,
+    // with the generated step, the K tiles of all slots in the first half of
+    // the ring and the V tiles in the second (every read then reaches its
+    // slot with a 16-bit immediate)
+    auto koff_of = [&](int st) { return ASM ? st * T::TILEB : st * 2 * T::TILEB; };
+    auto voff_of = [&](int st) { return ASM ? st * T::TILEB : st * 2 * T::TILEB + T::TILEB; };
+    // LDS byte at tile offset `off` of the slot at `slot_off` (ASM: `off` holds the address)
+    typedef __attribute__((address_space(3))) uint8_t lds_byte;
+    auto at = [&](int slot_off, int off) __attribute__((always_inline)) -> const uint8_t * {
+        if constexpr (ASM)
+            return (const uint8_t *)(const lds_byte *)(uintptr_t)(uint32_t)(off + slot_off);
+        else
+            return smem + slot_off + off;
+    };
 
     // ---- Q fragments: B operands of S^T = K Q^T (lane: query lr of each block)
     bf16x8 qf[QB][D / 16];
@@ -277,13 +310,12 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
 
     // S^T = K_t Q^T from ring slot st; each K fragment serves all QB query blocks
     auto scores = [&](int st, f32x16 (&acc)[QB][KB]) {
-        const uint8_t *kbase = smem + st * 2 * T::TILEB;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             bf16x8 a[D / 16];
 #pragma unroll
             for (int ds = 0; ds < D / 16; ++ds)
-                a[ds] = *(const bf16x8 *)(kbase + kb * 32 * T::ROWB + koff[ds]);
+                a[ds] = *(const bf16x8 *)at(koff_of(st) + kb * 32 * T::ROWB, koff[ds]);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
@@ -389,8 +421,8 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     // A operand of O^T += V_u^T P^T for k-step ks and rows 32b.. of V_u^T, read
     // transposed from the row-major V tile in the k-slot order of P^T
     auto vfrag = [&](int u, int ks, int b) {
-        const uint8_t *p = smem + (u % S) * 2 * T::TILEB + T::TILEB + ks * 16 * T::ROWB;
-        const u32x2 lo = tr_read(p + voff[b][0]), hi = tr_read(p + voff[b][1]);
+        const int so = voff_of(u % S) + ks * 16 * T::ROWB;
+        const u32x2 lo = tr_read(at(so, voff[b][0])), hi = tr_read(at(so, voff[b][1]));
         const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
         return __builtin_bit_cast(bf16x8, w);
     };
@@ -530,6 +562,73 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     const std::integral_constant<bool, false> plain;
     const std::integral_constant<bool, true> generic;
     int t = 0;
+    if constexpr (ASM) {
+        // The generated step (fwd128_step.inc) with this kernel's state in the
+        // registers it names.  It checks nothing itself: as in the generic
+        // steps, the tile maximum it leaves in mt is compared with the
+        // reference before the next step, which raises it in C++ (rare).  The
+        // accumulators are read by vector code only after a fence that gives
+        // the step's last products time to land.
+        auto fence = [&]() __attribute__((always_inline)) {
+            __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                             : "+{v[32:47]}"(oacc[0][0]), "+{v[48:63]}"(oacc[0][1]),
+                               "+{v[64:79]}"(oacc[0][2]), "+{v[80:95]}"(oacc[0][3]));
+        };
+#define FA_ASM_STEP(U)                                                                            \
+    __asm__ volatile(FA_FWD128_STEP_##U                                                           \
+                     : "+{v[32:47]}"(oacc[0][0]), "+{v[48:63]}"(oacc[0][1]),                      \
+                       "+{v[64:79]}"(oacc[0][2]), "+{v[80:95]}"(oacc[0][3]),                      \
+                       "+{v[96:111]}"(sacc[0][0]), "+{v[112:127]}"(snxt[0][0]),                   \
+                       "+{v184}"(l0[0]), "+{v185}"(l1[0]), "={v204}"(mt[0])                       \
+                     : [c] "s"(c), "{v[0:3]}"(qf[0][0]), "{v[4:7]}"(qf[0][1]),                    \
+                       "{v[8:11]}"(qf[0][2]), "{v[12:15]}"(qf[0][3]), "{v[16:19]}"(qf[0][4]),     \
+                       "{v[20:23]}"(qf[0][5]), "{v[24:27]}"(qf[0][6]), "{v[28:31]}"(qf[0][7]),    \
+                       "{v186}"(negm), "{v187}"(koff[0]), "{v188}"(koff[1]), "{v189}"(koff[2]),   \
+                       "{v190}"(koff[3]), "{v191}"(koff[4]), "{v192}"(koff[5]), "{v193}"(koff[6]), \
+                       "{v194}"(koff[7]), "{v195}"(voff[0][0]), "{v196}"(voff[0][1]), "{v197}"(voff[1][0]), \
+                       "{v198}"(voff[1][1]), "{v199}"(voff[2][0]), "{v200}"(voff[2][1]), "{v201}"(voff[3][0]), \
+                       "{v202}"(voff[3][1])                                                          \
+                     : FA_ASM_TEMPS "v203", "memory")
+        // one asm step per ring slot, so that each has its slot in its
+        // immediates and the state stays in its registers from step to step
+        auto astep = [&](auto U) __attribute__((always_inline)) {
+            if (__any(mt[0] > m[0] + kMargin)) {
+                fence();
+                raise(0);
+            }
+            const float negm = -m[0];
+            constexpr int u = decltype(U)::value;
+            if constexpr (u == 0) FA_ASM_STEP(0);
+            else if constexpr (u == 1) FA_ASM_STEP(1);
+            else if constexpr (u == 2) FA_ASM_STEP(2);
+            else if constexpr (u == 3) FA_ASM_STEP(3);
+            else if constexpr (u == 4) FA_ASM_STEP(4);
+            else if constexpr (u == 5) FA_ASM_STEP(5);
+            else if constexpr (u == 6) FA_ASM_STEP(6);
+            else FA_ASM_STEP(7);
+        };
+#undef FA_ASM_STEP
+        for (; t + S < nfull; t += S) {  // tiles t .. t+8 need no mask; t = 0 (mod 8)
+            const int tb = t & ~(S - 1);   // t, with its low bits visible to the compiler
+            ring(tb);
+            astep(std::integral_constant<int, 0>());
+            ring(tb + 1);
+            astep(std::integral_constant<int, 1>());
+            ring(tb + 2);
+            astep(std::integral_constant<int, 2>());
+            ring(tb + 3);
+            astep(std::integral_constant<int, 3>());
+            ring(tb + 4);
+            astep(std::integral_constant<int, 4>());
+            ring(tb + 5);
+            astep(std::integral_constant<int, 5>());
+            ring(tb + 6);
+            astep(std::integral_constant<int, 6>());
+            ring(tb + 7);
+            astep(std::integral_constant<int, 7>());
+        }
+        fence();
+    }
     for (; t + 2 < nfull; t += 2) {  // tiles t .. t+2 need no mask; scores alternate
         ring(t);
         step(t, sacc, snxt, plain);
