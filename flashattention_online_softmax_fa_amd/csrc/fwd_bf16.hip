@@ -87,9 +87,6 @@
 #ifndef FA_FWD_DMA_ALT
 #define FA_FWD_DMA_ALT 1
 #endif
-// with FA_FWD_DMA_ALT: wave priority of the loading wave until the next
-// barrier (s_setprio), so that it catches up with its partner: 1.5 % faster
-// at causal d = 128, level at d = 64
 // Instruction-interleaving strategy the compiler applies to a step
 // (__builtin_amdgcn_iglp_opt; 2 is its pattern for matrix products mixed
 // with exponentials), -1 for none: 0.7 % faster at d = 64 with 0 and 0.8 %
@@ -102,11 +99,14 @@
 #endif
 // 1: the mask-free steps of the d = 128 forward (one 32-query block per wave,
 // 32-key tiles, 8 ring slots) run the generated assembly of fwd128_step.inc,
-// with its own instruction order (0.5 % faster than the compiler's step at
-// causal d = 128, where the LDS read rate sets the pace)
+// with its own instruction order and the first K fragments of each step read
+// by the step before (1.5 % faster than the compiler's step at causal d = 128)
 #ifndef FA_FWD_ASM128
 #define FA_FWD_ASM128 1
 #endif
+// with FA_FWD_DMA_ALT: wave priority of the loading wave until the next
+// barrier (s_setprio), so that it catches up with its partner: 1.5 % faster
+// at causal d = 128, level at d = 64
 #ifndef FA_FWD_PRIO
 #define FA_FWD_PRIO 1
 #endif
@@ -163,6 +163,13 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     constexpr int KB = BC / 32;  // 32-key blocks per tile
     // the generated mask-free step (fwd128_step.inc) for this configuration
     constexpr bool ASM = FA_FWD_ASM128 && D == 128 && QB == 1 && BC == 32 && S == 8 && W == 8 && POS_SCALE;
+    // Ring lead: the loads issued at the barrier of step t are for tiles
+    // t+LEAD+1 .. t+LEAD+GR.  LEAD = GR publishes tile t+1 by step t; the
+    // generated step also reads part of tile t+2 in step t, which takes
+    // LEAD = 2 GR (the slots of tiles t-GR .. t-1, refilled at that barrier,
+    // then hold tiles t+LEAD+1 .. t+LEAD+GR, so S >= LEAD + GR + 2).
+    constexpr int LEAD = ASM ? 2 * GR : GR;
+    static_assert(GR == 1 || S >= LEAD + GR + 2, "ring depth for the lead");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[S * 2 * T::TILEB];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -520,7 +527,7 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
                 if (FA_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
                 if (((t / GR) & 1) != (wave >> 2)) return;
 #pragma unroll
-                for (int j = GR + 1; j <= 2 * GR; ++j)
+                for (int j = LEAD + 1; j <= LEAD + GR; ++j)
                     if (t + j < nkt) {
                         issue_as(t + j, (t + j) % S, 0);
                         issue_as(t + j, (t + j) % S, 1);
@@ -530,7 +537,7 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
                 return;
             }
 #pragma unroll
-            for (int j = GR + 1; j <= 2 * GR; ++j)
+            for (int j = LEAD + 1; j <= LEAD + GR; ++j)
                 if (t + j < nkt) issue(t + j, (t + j) % S);
         } else {
             if (t + 1 < nkt) {
@@ -542,12 +549,17 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         }
     };
 
-    constexpr int PRO = GR > 1 ? GR + 1 : S - 1;  // tiles issued before the loop
+    constexpr int PRO = GR > 1 ? LEAD + 1 : S - 1;  // tiles issued before the loop
 #pragma unroll
     for (int t = 0; t < PRO; ++t)
         if (t < nkt) issue(t, t);
     if (nkt > 0) {
-        wait_steps<T::LPW, PRO - 1>(nkt - 1 < PRO - 1 ? nkt - 1 : PRO - 1);  // tile 0 has landed
+        if constexpr (ASM) {  // tiles 0 and 1 have landed
+            const int rest = (nkt < PRO ? nkt : PRO) - 2;
+            wait_steps<T::LPW, PRO - 2>(rest < 0 ? 0 : rest);
+        } else {  // tile 0 has landed
+            wait_steps<T::LPW, PRO - 1>(nkt - 1 < PRO - 1 ? nkt - 1 : PRO - 1);
+        }
         lds_barrier();
         if (nkt_w > 0) {
             scores(0, sacc);
@@ -569,6 +581,11 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
         // reference before the next step, which raises it in C++ (rare).  The
         // accumulators are read by vector code only after a fence that gives
         // the step's last products time to land.
+        // K fragments 0-3 of tile t+1, read by the step before (for the first
+        // step, here: tiles 0 and 1 have landed)
+        u32x4 kf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kf[i] = *(const u32x4 *)at(koff_of(1), koff[i]);
         auto fence = [&]() __attribute__((always_inline)) {
             __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
                              : "+{v[32:47]}"(oacc[0][0]), "+{v[48:63]}"(oacc[0][1]),
@@ -579,7 +596,9 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
                      : "+{v[32:47]}"(oacc[0][0]), "+{v[48:63]}"(oacc[0][1]),                      \
                        "+{v[64:79]}"(oacc[0][2]), "+{v[80:95]}"(oacc[0][3]),                      \
                        "+{v[96:111]}"(sacc[0][0]), "+{v[112:127]}"(snxt[0][0]),                   \
-                       "+{v184}"(l0[0]), "+{v185}"(l1[0]), "={v204}"(mt[0])                       \
+                       "+{v184}"(l0[0]), "+{v185}"(l1[0]), "={v204}"(mt[0]),                      \
+                       "+{v[128:131]}"(kf[0]), "+{v[132:135]}"(kf[1]), "+{v[136:139]}"(kf[2]),    \
+                       "+{v[140:143]}"(kf[3])                                                     \
                      : [c] "s"(c), "{v[0:3]}"(qf[0][0]), "{v[4:7]}"(qf[0][1]),                    \
                        "{v[8:11]}"(qf[0][2]), "{v[12:15]}"(qf[0][3]), "{v[16:19]}"(qf[0][4]),     \
                        "{v[20:23]}"(qf[0][5]), "{v[24:27]}"(qf[0][6]), "{v[28:31]}"(qf[0][7]),    \

@@ -5,10 +5,13 @@ assembly with its own instruction order.
 Run  python gen_fwd128_step.py  to rewrite fwd128_step.inc beside it (the output is committed).
 
 The step of tile t (ring slot u = t % 8):
-  S^T of tile t+1 = K Q^T  (8 v_mfma_f32_32x32x16_bf16 over d, K from slot u+1),
+  S^T of tile t+1 = K Q^T  (8 v_mfma_f32_32x32x16_bf16 over d, K from slot u+1;
+                           its first 4 fragments were read by the previous step),
   P = exp2(S c - m) of tile t, in place, with the row sums and the bf16 packing,
   O^T += V^T P^T           (8 products, V^T from slot u read transposed),
-  the lane maximum of tile t+1's scores (times c) for the next step's check.
+  the lane maximum of tile t+1's scores (times c) for the next step's check,
+  the first 4 K fragments of tile t+2 (slot u+2) for the next step, read under
+  the PV products so that a step starts with its first product.
 The order interleaves the score products with the exponentials and reads each
 LDS operand well before its product; s_waitcnt and s_nop are placed by the
 rules below (the compiler does not see into inline assembly):
@@ -21,8 +24,9 @@ V tiles in the second, so that one base register per read and a 16-bit
 immediate reach every slot.  Registers are fixed (the kernel binds its
 variables to them):
   v[0:31] Q fragments, v[32:95] O accumulators, v[96:111] and v[112:127] the two
-  score sets, v[128:183] temporaries (4 K fragments, reused, 8 V^T fragments,
-  2 P^T fragments), v184/v185 row sums, v186 = -m, v[187:194] LDS addresses of
+  score sets, v[128:143] 4 K fragments (reused; they carry the first 4 of the
+  next tile from step to step), v[144:183] temporaries (8 V^T fragments, 2 P^T
+  fragments), v184/v185 row sums, v186 = -m, v[187:194] LDS addresses of
   the K reads, v[195:202] of the V^T reads (+64 KiB), v203 scratch, v204 the
   lane maximum.
 """
@@ -65,8 +69,11 @@ def step_ops(u):
     kimm = ((u + 1) % 8) * TILEB   # K of tile t+1
     vimm = u * TILEB               # V of tile t (the V registers hold the +64 KiB)
     ops = {}
+    kpre = ((u + 2) % 8) * TILEB   # K of tile t+2, the first half read ahead for the next step
     for k in range(8):
         ops[f"rk{k}"] = Ins("ds", f"ds_read_b128 {KF(k)}, {KOFF(k)} offset:{kimm}", [KF(k)], [KOFF(k)])
+    for k in range(4):
+        ops[f"pk{k}"] = Ins("ds", f"ds_read_b128 {KF(k)}, {KOFF(k)} offset:{kpre}", [KF(k)], [KOFF(k)])
     for ks in range(2):
         for b in range(4):
             for h in range(2):
@@ -105,7 +112,7 @@ def order():
     exponential before the first PV product; the maximum of the next tile after
     its last score product, under the PV products."""
     vre = [f"rv{ks}{b}{h}" for ks in range(2) for b in range(4) for h in range(2)]
-    o = ["rk0", "rk1", "rk2", "rk3"] + vre[:4]
+    o = vre[:4]   # K fragments 0-3 of tile t+1 were read by the previous step
     el = iter(range(16))
     for k in range(8):
         o += [f"s{k}"]
@@ -122,6 +129,8 @@ def order():
     for n in range(8):
         o += [pv[n]]
         o += mx[n:n + 1] if n < 7 else mx[7:]
+        if n < 4:  # K fragment n of tile t+2; its register was last read 4 products ago
+            o += [f"pk{n}"]
     return o
 
 
@@ -186,8 +195,8 @@ def render():
     for u in range(8):
         body = "\\n\\t".join(emit(order(), step_ops(u)))
         parts.append(f'#define FA_FWD128_STEP_{u} "{body}"\n')
-    temps = ", ".join(f'"v{r}"' for r in range(128, 184))
-    parts.append(f"// the step's temporaries: K and V^T fragments, P^T\n#define FA_ASM_TEMPS {temps},\n")
+    temps = ", ".join(f'"v{r}"' for r in range(144, 184))
+    parts.append(f"// the step's temporaries: V^T fragments, P^T\n#define FA_ASM_TEMPS {temps},\n")
     return "\n".join(parts)
 
 

@@ -104,10 +104,18 @@ def test_step_reads_its_slot(u):
     ops = [_parse(x) for x in _steps()[u]]
     k_offs = sorted(o for op, _, _, o in ops if op == "ds_read_b128")
     v_offs = sorted(o for op, _, _, o in ops if op == "ds_read_b64_tr_b16")
-    # K of the next tile (slot u+1), V of this tile (slot u), each in its half of the ring
-    assert k_offs == [((u + 1) % 8) * TILEB] * 8
+    # K of the next tile (slot u+1: fragments 4-7, the first 4 carried in from
+    # the step before) and of the one after (slot u+2: fragments 0-3 for the
+    # next step), V of this tile (slot u), each in its half of the ring
+    assert k_offs == sorted([((u + 1) % 8) * TILEB] * 4 + [((u + 2) % 8) * TILEB] * 4)
     assert v_offs == sorted([u * TILEB] * 8 + [u * TILEB + 16 * ROWB] * 8)
     assert all(o < 1 << 16 for o in k_offs + v_offs)
+    # fragments 0-3 of the next tile are read only after the last product that
+    # reads the registers they land in
+    lines = [_parse(x) for x in _steps()[u]]
+    last_s = max(i for i, (op, d, _, _) in enumerate(lines) if op.startswith("v_mfma") and d == set(range(96 + 16 * (1 - u % 2), 112 + 16 * (1 - u % 2))))
+    pre = [i for i, (op, _, _, o) in enumerate(lines) if op == "ds_read_b128" and o == ((u + 2) % 8) * TILEB]
+    assert min(pre) > last_s
     mfma = [(d, s) for op, d, s, _ in ops if op.startswith("v_mfma")]
     assert len(mfma) == 16
     cur, nxt = set(range(96 + 16 * (u % 2), 112 + 16 * (u % 2))), set(range(96 + 16 * (1 - u % 2), 112 + 16 * (1 - u % 2)))
