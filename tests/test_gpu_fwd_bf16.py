@@ -160,6 +160,30 @@ def test_rising_scores(fa, d, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_rising_scores_long_d128(fa, causal):
+    """The rising scores of test_rising_scores over 700 keys at d = 128, so
+    that the raise happens inside the mask-free stretches (runs of 9 or more
+    unmasked key tiles) that the d = 128 kernel steps through in groups of 8,
+    under causal as well (every wave of the later query tiles)."""
+    d, B, H, N = 128, 1, 2, 700
+    x = make_inputs(B, H, N, N, d, "bf16", seed=91 + (causal is True), device="cpu")
+    scale = 1 / math.sqrt(d)
+    c = scale / math.log(2)
+    q = x.q.float() * 0.1
+    k = x.k.float() * 0.1
+    q[..., 0] = torch.where(torch.arange(N) % 2 == 0, 1.0, -1.0)
+    k[..., 0] = torch.arange(N, dtype=torch.float32) / c
+    qb, kb = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    say(f"bf16 fwd rising scores over {N} keys d={d} causal={causal}")
+    o, lse = fa.forward(qb.cuda(), kb.cuda(), x.v.cuda(), scale, causal)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.dense_fwd(host(qb), host(kb), host(x.v), scale, causal)
+    assert float(np.abs(L_ref).max()) > 400
+    assert max_abs(o, O_ref) <= O_TOL
+    assert max_abs(lse, L_ref) <= L_TOL
+
+
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 def test_long_sequence_sampled(fa, d, causal):
     """One head of 65536 queries and keys: 2048 key tiles per wave, the K/V
