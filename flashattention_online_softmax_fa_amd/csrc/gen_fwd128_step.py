@@ -19,6 +19,10 @@ rules below (the compiler does not see into inline assembly):
   * a matrix-core result is read by vector code >= 18 wait states later;
   * a vector result feeds a matrix-core operand >= 2 wait states later;
   * a transcendental result feeds vector code >= 1 wait state later.
+(The wait-state counts follow the data-hazard tables of AMD's public CDNA3
+instruction-set reference for 16-pass matrix instructions, which gfx950
+keeps; the GPU parity tests check the result.)  Products chained on one
+accumulator need no waits: the matrix pipe forwards srcC between them.
 The ring keeps the K tiles of its 8 slots in the first 64 KiB of LDS and the
 V tiles in the second, so that one base register per read and a 16-bit
 immediate reach every slot.  Registers are fixed (the kernel binds its
