@@ -171,6 +171,7 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     constexpr int LEAD = ASM ? 2 * GR : GR;
     static_assert(GR == 1 || S >= LEAD + GR + 2, "ring depth for the lead");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[S * 2 * T::TILEB];
+    __shared__ __attribute__((aligned(16))) uint8_t ostage[W * 4096];  // per-wave O staging
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -666,26 +667,46 @@ void fwd_bf16_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
     }
     wait_vm<0>();
 
-    // ---- epilogue: one division, natural-log L
+    // ---- epilogue: one division, natural-log L.  A lane holds 4-value pieces
+    // of one query's O row (column lr of O^T), so O leaves through this wave's
+    // own 4 KiB of LDS, 32 rows x 64 columns at a time: each global store then
+    // writes 8 rows x 128 contiguous bytes instead of 32 rows x 16 bytes.
+    // Row r's 16-byte chunk c sits at chunk c ^ (r % 8) of its 128 bytes.
+    uint8_t *stg = ostage + wave * 4096;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int64_t qrow = qw0 + 32 * qb + lr;
         const float lh = l0[qb] + l1[qb];
         const float l_tot = lh + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
                                      xaddr, __builtin_bit_cast(int, lh)));
-        if (qrow < Nq) {
-            const float inv = 1.f / l_tot;
-            uint16_t *orow = O + (bh * Nq + qrow) * D;
+        const float inv = 1.f / l_tot;
+        if (qrow < Nq && g == 0) L[bh * Nq + qrow] = (m[qb] + log2f(l_tot)) * kLn2;
 #pragma unroll
-            for (int b = 0; b < D / 32; ++b)
+        for (int h = 0; h < D / 64; ++h) {
+#pragma unroll
+            for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
                 for (int t4 = 0; t4 < 4; ++t4) {
+                    const int b = 2 * h + b2;
                     const u32x2 w = {
                         pack_bf16x2(oacc[qb][b][4 * t4] * inv, oacc[qb][b][4 * t4 + 1] * inv),
                         pack_bf16x2(oacc[qb][b][4 * t4 + 2] * inv, oacc[qb][b][4 * t4 + 3] * inv)};
-                    *(u32x2 *)(orow + b * 32 + 8 * t4 + 4 * g) = w;
+                    *(u32x2 *)(stg + lr * 128 + (((4 * b2 + t4) ^ (lr & 7)) << 4) + 8 * g) = w;
                 }
-            if (g == 0) L[bh * Nq + qrow] = (m[qb] + log2f(l_tot)) * kLn2;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 8 * i + (lane >> 3), ch = lane & 7;
+                const u32x4 w = *(const u32x4 *)(stg + r * 128 + ((ch ^ (r & 7)) << 4));
+                const int64_t orow = qw0 + 32 * qb + r;
+                if (orow < Nq) *(u32x4 *)(O + (bh * Nq + orow) * D + 64 * h + 8 * ch) = w;
+            }
+            // the next piece overwrites the stage only after these reads
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
 #if FA_STATS
