@@ -114,11 +114,11 @@
 namespace fa {
 namespace {
 
-constexpr float kMargin = 8.f;
+constexpr float kMargin = 8.f;  // base-2 headroom before the reference max is raised
 
 #if FA_STATS
 __device__ unsigned long long g_fwd_stats[kStatCount];
-#endif         // base-2 headroom before the reference max is raised
+#endif
 
 // D: head dimension; QB: 32-query blocks per wave (each K / V^T fragment read
 // from LDS feeds QB matrix-core products); BC: keys per tile; W: waves per
