@@ -380,28 +380,17 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
 #if FA_STATS
     if (lane == 0 && kw0 < Nk) atomicAdd(&g_bwd_stats[3], (unsigned long long)st_tiles);
 #endif
-    // ---- epilogue: dK = scale * dK_acc, dV = dV_acc (lane: key lr of block kb;
-    //      register r: column 32b + 8*(r/4) + 4g + r%4)
+    // ---- epilogue: dK = scale * dK_acc, dV = dV_acc, each 32-key block
+    //      through 4 KiB of LDS per tensor (store_rows_staged); every wave is
+    //      past its last ring read at the barrier, so the ring holds the stages
+    static_assert(ST * T::STAGEB >= W * 8192, "the ring holds the output stages");
+    wait_vm<0>();
+    lds_barrier();
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-        const int64_t key = kw0 + 32 * kb + lr;
-        if (key < Nk) {
-            uint16_t *dKr = dK + (bh * Nk + key) * D;
-            uint16_t *dVr = dV + (bh * Nk + key) * D;
-#pragma unroll
-            for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int col = b * 32 + 8 * t + 4 * g;
-                    const f32x16 &ka = dkacc[kb][b], &va = dvacc[kb][b];
-                    const u32x2 wk = {pack_bf16x2(scale * ka[4 * t], scale * ka[4 * t + 1]),
-                                      pack_bf16x2(scale * ka[4 * t + 2], scale * ka[4 * t + 3])};
-                    const u32x2 wv = {pack_bf16x2(va[4 * t], va[4 * t + 1]),
-                                      pack_bf16x2(va[4 * t + 2], va[4 * t + 3])};
-                    *(u32x2 *)(dKr + col) = wk;
-                    *(u32x2 *)(dVr + col) = wv;
-                }
-        }
+        store_rows_staged<D>(smem + wave * 8192, dkacc[kb], scale, dK + bh * Nk * D, kw0 + 32 * kb, Nk, lane);
+        store_rows_staged<D>(smem + wave * 8192 + 4096, dvacc[kb], 1.f, dV + bh * Nk * D, kw0 + 32 * kb, Nk,
+                             lane);
     }
 }
 
@@ -667,26 +656,14 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
 #if FA_STATS
     if (lane == 0 && kw0 < Nk) atomicAdd(&g_bwd_stats[3], (unsigned long long)st_tiles);
 #endif
-    // ---- epilogue: dK = scale * dK_acc, dV = dV_acc (lane: key lr; register
-    //      r: column 32b + 8*(r/4) + 4g + r%4)
-    const int64_t key = kw0 + lr;
-    if (key < Nk) {
-        uint16_t *dKr = dK + (bh * Nk + key) * D;
-        uint16_t *dVr = dV + (bh * Nk + key) * D;
-#pragma unroll
-        for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int col = b * 32 + 8 * t + 4 * g;
-                const f32x16 &ka = dkacc[b], &va = dvacc[b];
-                const u32x2 wk = {pack_bf16x2(scale * ka[4 * t], scale * ka[4 * t + 1]),
-                                  pack_bf16x2(scale * ka[4 * t + 2], scale * ka[4 * t + 3])};
-                const u32x2 wv = {pack_bf16x2(va[4 * t], va[4 * t + 1]),
-                                  pack_bf16x2(va[4 * t + 2], va[4 * t + 3])};
-                *(u32x2 *)(dKr + col) = wk;
-                *(u32x2 *)(dVr + col) = wv;
-            }
-    }
+    // ---- epilogue: dK = scale * dK_acc, dV = dV_acc through 4 KiB of LDS per
+    //      tensor (store_rows_staged); every wave is past its last ring read at
+    //      the barrier, so the ring holds the stages
+    static_assert(ST * T::STAGEB >= W * 8192, "the ring holds the output stages");
+    wait_vm<0>();
+    lds_barrier();
+    store_rows_staged<D>(smem + wave_u * 8192, dkacc, scale, dK + bh * Nk * D, kw0, Nk, lane);
+    store_rows_staged<D>(smem + wave_u * 8192 + 4096, dvacc, 1.f, dV + bh * Nk * D, kw0, Nk, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -955,24 +932,15 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 #if FA_STATS
     if (lane == 0 && qw0 < Nq) atomicAdd(&g_bwd_stats[4], (unsigned long long)st_tiles);
 #endif
-    // ---- epilogue: dQ = scale * acc (lane: query lr of block qb; register r:
-    //      column 32b + 8*(r/4) + 4g + r%4)
+    // ---- epilogue: dQ = scale * acc through 4 KiB of LDS (store_rows_staged);
+    //      every wave is past its last ring read at the barrier, so the ring
+    //      holds the stages
+    static_assert(ST * 2 * T::TILEB >= W * 4096, "the ring holds the output stages");
+    wait_vm<0>();
+    lds_barrier();
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int64_t qrow = qw0 + 32 * qb + lr;
-        if (qrow < Nq) {
-            uint16_t *row = dQ + (bh * Nq + qrow) * D;
-#pragma unroll
-            for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const f32x16 &a = acc[qb][b];
-                    const u32x2 w = {pack_bf16x2(scale * a[4 * t], scale * a[4 * t + 1]),
-                                     pack_bf16x2(scale * a[4 * t + 2], scale * a[4 * t + 3])};
-                    *(u32x2 *)(row + b * 32 + 8 * t + 4 * g) = w;
-                }
-        }
-    }
+    for (int qb = 0; qb < QB; ++qb)
+        store_rows_staged<D>(smem + wave * 4096, acc[qb], scale, dQ + bh * Nq * D, qw0 + 32 * qb, Nq, lane);
 }
 
 // Tile configurations (chosen by measurement on MI355X).

@@ -34,6 +34,50 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Order this wave's LDS accesses before and after (another lane's data is read
+// back through LDS).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Writes a 32-row x D-column bf16 tile whose fp32 values the wave holds as
+// transposed 32x32 matrix-core results: lane l has row l % 32, and register
+// 4t + k of block b is column 32b + 8t + 4(l / 32) + k.  Each value is
+// multiplied by s and rounded; row r goes to dst + (row0 + r) * D, rows at or
+// past nrows are skipped.  A lane holds 4-column pieces of a single row, so
+// the tile passes through a 4 KiB LDS stage of this wave, 32 rows x 64
+// columns at a time (row r's 16-byte chunk c at chunk c ^ (r % 8) of its 128
+// bytes): each store then writes 8 rows x 128 contiguous bytes instead of
+// 32 rows x 16 bytes.
+template <int D>
+__device__ __forceinline__ void store_rows_staged(uint8_t *stg, const f32x16 *acc, float s,
+                                                  uint16_t *dst, int64_t row0, int64_t nrows,
+                                                  int lane) {
+    const int lr = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int h = 0; h < D / 64; ++h) {
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const f32x16 &a = acc[2 * h + b2];
+                const u32x2 w = {pack_bf16x2(a[4 * t] * s, a[4 * t + 1] * s),
+                                 pack_bf16x2(a[4 * t + 2] * s, a[4 * t + 3] * s)};
+                *(u32x2 *)(stg + lr * 128 + (((4 * b2 + t) ^ (lr & 7)) << 4) + 8 * g) = w;
+            }
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 8 * i + (lane >> 3), ch = lane & 7;
+            const u32x4 w = *(const u32x4 *)(stg + r * 128 + ((ch ^ (r & 7)) << 4));
+            if (row0 + r < nrows) *(u32x4 *)(dst + (row0 + r) * D + 64 * h + 8 * ch) = w;
+        }
+        wave_lds_sync();  // the next piece overwrites the stage only after these reads
+    }
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

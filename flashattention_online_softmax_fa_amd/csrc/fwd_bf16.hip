@@ -146,7 +146,7 @@ struct Tile {
     static_assert(LPW >= 1 && LPW * W == 2 * NB, "K and V tiles split evenly over the waves");
     static_assert(G == 1 || G == 2 || G == 4 || G == 8, "tiles per barrier");
     static_assert(STAGES >= (G == 1 ? 3 : 2 * G + 1) && STAGES <= 20, "ring depth");
-    static_assert(STAGES * 2 * TILEB <= 160 * 1024, "ring fits the 160 KiB LDS");
+    static_assert(STAGES * 2 * TILEB + W * 4096 <= 160 * 1024, "ring and O stages fit the 160 KiB LDS");
     static_assert(BC % 32 == 0, "32-key blocks");
     static_assert(W == 4 || W == 8, "4 or 8 waves");
 };
