@@ -63,13 +63,18 @@ KERNEL_SOURCES = {
 
 
 def source_hash(name: str) -> str:
-    """Hash of a kernel source and the device headers it includes, with
+    """Hash of a kernel source, the device headers and the generated code it includes, with
     comments and white space removed: measured traffic stays valid across
     changes to comments and layout, and lapses with any change to the code."""
     import re
+    csrc = os.path.join(ROOT, "flashattention_online_softmax_fa_amd", "csrc")
+    with open(os.path.join(csrc, name)) as fh:
+        src = fh.read()
+    # generated code it includes (the d = 128 forward step) counts as its code
+    incs = re.findall(r'#include "([\w.]+\.inc)"', src)
     text = ""
-    for f in (name, "fa_device.h", "fa_internal.h"):
-        with open(os.path.join(ROOT, "flashattention_online_softmax_fa_amd", "csrc", f)) as fh:
+    for f in [name, "fa_device.h", "fa_internal.h"] + incs:
+        with open(os.path.join(csrc, f)) as fh:
             text += fh.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
