@@ -349,3 +349,22 @@ def test_traffic_hash_ignores_comments_only(tmp_path):
     d = dst / "fa_device.h"
     d.write_text(d.read_text().replace("kLog2e = 1.4426950408889634f", "kLog2e = 1.4426950408889635f"))
     assert bench.source_hash("bwd.hip") != h0
+
+
+def test_traffic_hash_covers_generated_step(tmp_path):
+    """The forward's hash changes when the generated step it includes changes."""
+    import importlib.util
+    import shutil
+    spec = importlib.util.spec_from_file_location("bench_mod3", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    src = os.path.join(ROOT, "flashattention_online_softmax_fa_amd", "csrc")
+    dst = tmp_path / "flashattention_online_softmax_fa_amd" / "csrc"
+    dst.mkdir(parents=True)
+    for f in ("fwd_bf16.hip", "fa_device.h", "fa_internal.h", "fwd128_step.inc"):
+        shutil.copy(os.path.join(src, f), dst / f)
+    bench.ROOT = str(tmp_path)
+    h0 = bench.source_hash("fwd_bf16.hip")
+    p = dst / "fwd128_step.inc"
+    p.write_text(p.read_text().replace("s_waitcnt lgkmcnt(0)", "s_waitcnt lgkmcnt(1)", 1))
+    assert bench.source_hash("fwd_bf16.hip") != h0
