@@ -20,8 +20,9 @@
 //   bwd_dkdv_kernel  one workgroup per (batch*head, key tile), W waves of 32
 //                    keys, K and V in registers; Q, dO, L2 and -D tiles of the
 //                    query tiles that can see its keys stream through an LDS ring
-//                    (d = 64: bwd_dkdv_pipe_kernel, the same work software-
-//                    pipelined over 32-query tiles).
+//                    (by default bwd_dkdv_pipe_kernel, the same work software-
+//                    pipelined over 32-query tiles: eight waves at d = 64, four
+//                    at d = 128).
 // Both passes start the dP accumulators from -D, so that the products leave
 // dP - D and dS = P (dP - D) takes one multiply.
 // Both rings are filled with global_load_lds_dwordx4 into row-major,
@@ -418,12 +419,13 @@ struct DkdvPipeCfg {
     static constexpr int STAGEB = 2 * TILEB + 2 * VECB;
     static constexpr int GR = GR_;                 // query tiles per LDS barrier
     static constexpr int ST = 2 * GR + 1;          // ring slots
-    static_assert(2 * NB == W, "one 1 KiB load per wave per tile");
+    static constexpr int LPW = 2 * NB / W;         // 1 KiB loads per wave per tile
+    static_assert(LPW >= 1 && LPW * W == 2 * NB, "the tile's loads split evenly over the waves");
     static_assert(GR >= 1 && ST * STAGEB <= 160 * 1024, "ring fits the 160 KiB LDS");
 };
 
 template <int D, int GR, int W, bool CAUSAL>
-__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W / 4, W / 4)))
 void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                           const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
                           const float *__restrict__ L2, const float *__restrict__ Dv,
@@ -453,19 +455,24 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
         vf[ds] = __builtin_bit_cast(bf16x8, load_row16(V + bh * Nk * D, kw0 + lr, Nk, D, ds * 2 + g));
     }
 
-    // ---- ring loads: load j of a tile (one per wave) fills 1 KiB block j of
-    //      the stage (Q blocks, then dO blocks); this lane writes chunk `lane`
-    //      of the block, i.e. row (j % NB)*RPI + lane/CH of its tile with
-    //      logical chunk (lane % CH) ^ swz(row).  Loads 0 and 1 also fill the
-    //      L2 and -D slices.  With FA_BWD_DMA_ALT, wave w also issues the load
-    //      of its partner w ^ 4, one barrier in two.
+    // ---- ring loads: load j of a tile fills 1 KiB block j of the stage (Q
+    //      blocks, then dO blocks); this lane writes chunk `lane` of the block,
+    //      i.e. row (j % NB)*RPI + lane/CH of its tile with logical chunk
+    //      (lane % CH) ^ swz(row).  Loads 0 and 1 also fill the L2 and -D
+    //      slices.  Wave w owns loads LPW*w .. LPW*w + LPW-1 (one at d = 64
+    //      with eight waves, four at d = 128 with four); with FA_BWD_DMA_ALT
+    //      (eight waves) wave w also issues the load of its partner w ^ 4, one
+    //      barrier in two.
     constexpr bool ALT = FA_BWD_DMA_ALT && W == 8;
-    const uint32_t owner_u[2] = {wave_u, wave_u ^ 4u};
-    uint32_t ld_off[2];
+    constexpr int LPW = T::LPW, NO = ALT ? 2 : LPW;
+    static_assert(!ALT || LPW == 1, "partner loads with one load per wave");
+    uint32_t owner_u[NO], ld_off[NO];
 #pragma unroll
-    for (int o = 0; o < 2; ++o)
+    for (int o = 0; o < NO; ++o) {
+        owner_u[o] = ALT ? (o == 0 ? wave_u : wave_u ^ 4u) : wave_u * LPW + o;
         ld_off[o] = (uint32_t)chunk_off<ROWB>((int)(owner_u[o] % T::NB) * T::RPI + lane / T::CH,
                                               lane % T::CH);
+    }
     // (scalar bases at the tile and 32-bit lane offsets; rows and vector
     // lanes past Nq re-read row Nq-1, masked later)
     auto issue_as = [&](int it, int st, int o) __attribute__((always_inline)) {
@@ -597,8 +604,8 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
 #pragma unroll
         for (int t = GR + 1; t <= 2 * GR; ++t)
             if (it0 + idx + t < nqt) {
-                issue_as(it0 + idx + t, (idx + t) % ST, 0);
-                if (ALT) issue_as(it0 + idx + t, (idx + t) % ST, 1);
+#pragma unroll
+                for (int o = 0; o < NO; ++o) issue_as(it0 + idx + t, (idx + t) % ST, o);
             }
         // the loading wave is behind its partner: let it catch up
         if (ALT && FA_BWD_PRIO) __builtin_amdgcn_s_setprio(FA_BWD_PRIO);
@@ -610,7 +617,10 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
     f32x16 s0, p0, s1, p1;
 #pragma unroll
     for (int t = 0; t <= GR; ++t)
-        if (it0 + t < nqt) issue_as(it0 + t, t, 0);
+        if (it0 + t < nqt) {
+#pragma unroll
+            for (int o = 0; o < LPW; ++o) issue_as(it0 + t, t, o);  // own loads only
+        }
     wait_vm<0>();
     lds_barrier();
 
@@ -989,6 +999,13 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 #ifndef FA_BWD_GR_PIPE  // its query tiles per LDS barrier
 #define FA_BWD_GR_PIPE 8
 #endif
+// the same at d = 128 (query tiles per barrier: 4, a 9-slot ring of 16.5 KiB stages)
+#ifndef FA_BWD_DKDV_PIPE128
+#define FA_BWD_DKDV_PIPE128 1
+#endif
+#ifndef FA_BWD_GR_PIPE128
+#define FA_BWD_GR_PIPE128 4
+#endif
 
 template <int D, bool CAUSAL>
 struct DkdvChoice {
@@ -1030,11 +1047,14 @@ hipError_t launch_main(const BwdArgs &a, hipStream_t s) {
                        a.scale, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if constexpr (D == 64 && FA_BWD_DKDV_PIPE) {
-        using P = DkdvPipeCfg<D, FA_BWD_GR_PIPE, 8>;
+    if constexpr (D == 64 ? FA_BWD_DKDV_PIPE : FA_BWD_DKDV_PIPE128) {
+        // d = 128: four waves (one per SIMD: K, V, both accumulators and two
+        // score sets take more than 256 registers)
+        constexpr int PW = D == 64 ? 8 : 4, PG = D == 64 ? FA_BWD_GR_PIPE : FA_BWD_GR_PIPE128;
+        using P = DkdvPipeCfg<D, PG, PW>;
         const int nkt = (int)((a.Nk + P::KEYS - 1) / P::KEYS);
-        hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<D, FA_BWD_GR_PIPE, 8, CAUSAL>),
-                           dim3((unsigned)(a.B * a.H * nkt)), dim3(8 * 64), 0, s,
+        hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<D, PG, PW, CAUSAL>),
+                           dim3((unsigned)(a.B * a.H * nkt)), dim3(PW * 64), 0, s,
                            (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
                            (const uint16_t *)a.dO, a.L2, a.D, (uint16_t *)a.dK, (uint16_t *)a.dV,
                            a.Nq, a.Nk, a.q_start, nkt, tile_group(a.B * a.H), a.scale,
