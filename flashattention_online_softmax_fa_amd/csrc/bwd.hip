@@ -701,7 +701,7 @@ struct DqCfg {
 };
 
 template <int D, int BC, int GR, int W, int QB, bool CAUSAL>
-__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(D == 64 ? FA_BWD_DQ_WPE : 2, D == 64 ? FA_BWD_DQ_WPE : 2)))
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(D == 64 ? FA_BWD_DQ_WPE : 3 - QB, D == 64 ? FA_BWD_DQ_WPE : 3 - QB)))
 void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                    const uint16_t *__restrict__ V, const uint16_t *__restrict__ O,
                    const uint16_t *__restrict__ dO, const float *__restrict__ L,
@@ -971,6 +971,9 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 #define FA_BWD_W_DKDV64 8
 #define FA_BWD_W_DQ64 8
 #endif
+#ifndef FA_BWD_DQ_QB128  // the same at d = 128 (2: one wave per SIMD)
+#define FA_BWD_DQ_QB128 1
+#endif
 #ifndef FA_BWD_DQ_QB64  // 32-query blocks per wave of the dQ pass, d = 64
 #define FA_BWD_DQ_QB64 1
 #endif
@@ -1029,7 +1032,7 @@ struct DqChoice {
     static constexpr int BC = D == 64 ? FA_BWD_DQ_BC64 : FA_BWD_DQ_BC128;
     static constexpr int W = D == 64 ? FA_BWD_W_DQ64 : FA_BWD_W_DQ128;
     static constexpr int GR = D == 64 ? FA_BWD_GR_DQ64 : FA_BWD_GR_DQ128;
-    static constexpr int QB = D == 64 ? FA_BWD_DQ_QB64 : 1;
+    static constexpr int QB = D == 64 ? FA_BWD_DQ_QB64 : FA_BWD_DQ_QB128;
     using Cfg = DqCfg<D, BC, GR, W, QB>;
 };
 
