@@ -406,11 +406,12 @@ void bwd_dkdv_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict_
 // The eight waves of a workgroup share one LDS ring of Q, dO, L2 and -D tiles:
 // a ring of 2*GR + 1 slots with one barrier per GR tiles (the barrier
 // publishes tiles t+1 .. t+GR and frees the slots of t-GR .. t-1).
-template <int D, int GR_, int W_>
+template <int D, int GR_, int W_, int KB_ = 1>
 struct DkdvPipeCfg {
     static constexpr int W = W_;                   // waves per workgroup
+    static constexpr int KB = KB_;                 // 32-key blocks per wave
     static constexpr int BR = 32;                  // queries per tile
-    static constexpr int KEYS = 32 * W;            // keys per workgroup
+    static constexpr int KEYS = 32 * KB * W;       // keys per workgroup
     static constexpr int CH = D / 8, ROWB = D * 2;
     static constexpr int TILEB = BR * ROWB;        // one Q or dO tile
     static constexpr int NB = TILEB / 1024;        // 1 KiB blocks per tile
@@ -424,14 +425,14 @@ struct DkdvPipeCfg {
     static_assert(GR >= 1 && ST * STAGEB <= 160 * 1024, "ring fits the 160 KiB LDS");
 };
 
-template <int D, int GR, int W, bool CAUSAL>
+template <int D, int GR, int W, int KB, bool CAUSAL>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W / 4, W / 4)))
 void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                           const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
                           const float *__restrict__ L2, const float *__restrict__ Dv,
                           uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int64_t Nq,
                           int64_t Nk, int64_t qoff, int nkt, uint32_t group, float scale, float c) {
-    using T = DkdvPipeCfg<D, GR, W>;
+    using T = DkdvPipeCfg<D, GR, W, KB>;
     constexpr int ST = T::ST, ROWB = T::ROWB, BR = T::BR;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * T::STAGEB];
 
@@ -441,19 +442,23 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
     const TileId tid_ = tile_order(blockIdx.x, gridDim.x / (uint32_t)nkt, (uint32_t)nkt, group);
     const int64_t bh = tid_.head;
     const int64_t k0 = (int64_t)tid_.rank * T::KEYS;  // causal: early keys are seen by the most queries
-    const int64_t kw0 = k0 + 32 * (int64_t)wave_u;     // this wave's keys: kw0 + lane%32
+    const int64_t kw0 = k0 + 32 * KB * (int64_t)wave_u;  // key block kb of this wave: kw0 + 32kb + lane%32
     const uint16_t *Qh = uniform_ptr(Q + bh * Nq * D);
     const uint16_t *dOh = uniform_ptr(dO + bh * Nq * D);
     const float *L2h = uniform_ptr(L2 + bh * Nq);
     const float *Dh = uniform_ptr(Dv + bh * Nq);
 
     // K and V of this wave's keys: B operands of S = Q K^T and dP = dO V^T
-    bf16x8 kf[D / 16], vf[D / 16];
+    // (each Q and dO fragment read from LDS serves the KB key blocks)
+    bf16x8 kf[KB][D / 16], vf[KB][D / 16];
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-        kf[ds] = __builtin_bit_cast(bf16x8, load_row16(K + bh * Nk * D, kw0 + lr, Nk, D, ds * 2 + g));
-        vf[ds] = __builtin_bit_cast(bf16x8, load_row16(V + bh * Nk * D, kw0 + lr, Nk, D, ds * 2 + g));
-    }
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) {
+            const int64_t key = kw0 + 32 * kb + lr;
+            kf[kb][ds] = __builtin_bit_cast(bf16x8, load_row16(K + bh * Nk * D, key, Nk, D, ds * 2 + g));
+            vf[kb][ds] = __builtin_bit_cast(bf16x8, load_row16(V + bh * Nk * D, key, Nk, D, ds * 2 + g));
+        }
 
     // ---- ring loads: load j of a tile fills 1 KiB block j of the stage (Q
     //      blocks, then dO blocks); this lane writes chunk `lane` of the block,
@@ -500,55 +505,70 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
 #pragma unroll
     for (int b = 0; b < D / 32; ++b) toff[b] = tr_off<ROWB>(lane, b, 0);
 
-    f32x16 dvacc[D / 32], dkacc[D / 32];
+    f32x16 dvacc[KB][D / 32], dkacc[KB][D / 32];
 #pragma unroll
-    for (int b = 0; b < D / 32; ++b)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            dvacc[b][r] = 0.f;
-            dkacc[b][r] = 0.f;
-        }
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                dvacc[kb][b][r] = 0.f;
+                dkacc[kb][b][r] = 0.f;
+            }
 
-    // S = Q K^T and dP - D = dO V^T - D of the tile in slot st (lane: key lr;
-    // register r: query 8*(r/4) + 4g + r%4 of the tile)
-    auto sdp = [&](int st, f32x16 &sa, f32x16 &pa) __attribute__((always_inline)) {
+    // S = Q K^T and dP - D = dO V^T - D of the tile in slot st (key block kb:
+    // lane: key 32kb + lr; register r: query 8*(r/4) + 4g + r%4 of the tile)
+    using Set = f32x16[KB];
+    auto sdp = [&](int st, Set &sa, Set &pa) __attribute__((always_inline)) {
         const uint8_t *qt = smem + st * T::STAGEB;
         const uint8_t *ot = qt + T::TILEB;
         const float *dt = (const float *)(ot + T::TILEB) + T::VECB / 4;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sa[r] = 0.f;
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sa[kb][r] = 0.f;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const f32x4 nd = *(const f32x4 *)(dt + 8 * r4 + 4 * g);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pa[4 * r4 + e] = nd[e];
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pa[kb][4 * r4 + e] = nd[e];
         }
 #pragma unroll
         for (int ds = 0; ds < D / 16; ++ds) {
             const bf16x8 aq = *(const bf16x8 *)(qt + roff[ds]);
             const bf16x8 ao = *(const bf16x8 *)(ot + roff[ds]);
-            sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ds], sa, 0, 0, 0);
-            pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[ds], pa, 0, 0, 0);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kb][ds], sa[kb], 0, 0, 0);
+                pa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[kb][ds], pa[kb], 0, 0, 0);
+            }
         }
     };
     // P = exp2(S c - L2), dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS
     // with the tile in slot st.  MASKED instances: query offset 8*(r/4) + 4g +
     // r%4 of register r is visible to this lane's key iff lo <= 8*(r/4) + r%4
     // <= hi (lo and hi less 4g, so that the offsets compared are constants)
-    auto finish = [&](int st, int64_t q0, f32x16 &sa, f32x16 &pa, auto masked)
+    auto finish = [&](int st, int64_t q0, Set &sa, Set &pa, auto masked)
                       __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked)::value;
         const uint8_t *qt = smem + st * T::STAGEB;
         const uint8_t *ot = qt + T::TILEB;
         const float *lt = (const float *)(ot + T::TILEB);
-        int lo = 0, hi = BR - 1;
-        if (MASKED) {
-            const int64_t key = kw0 + lr;
-            int64_t lo64 = CAUSAL ? key - qoff - q0 : 0;
-            int64_t hi64 = Nq - 1 - q0;
-            if (key >= Nk) hi64 = -1;
-            lo = (int)(lo64 < 0 ? 0 : (lo64 > BR ? BR : lo64)) - 4 * g;
-            hi = (int)(hi64 > BR - 1 ? BR - 1 : (hi64 < -1 ? -1 : hi64)) - 4 * g;
+        int lo[KB], hi[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            lo[kb] = 0;
+            hi[kb] = BR - 1;
+            if (MASKED) {
+                const int64_t key = kw0 + 32 * kb + lr;
+                int64_t lo64 = CAUSAL ? key - qoff - q0 : 0;
+                int64_t hi64 = Nq - 1 - q0;
+                if (key >= Nk) hi64 = -1;
+                lo[kb] = (int)(lo64 < 0 ? 0 : (lo64 > BR ? BR : lo64)) - 4 * g;
+                hi[kb] = (int)(hi64 > BR - 1 ? BR - 1 : (hi64 < -1 ? -1 : hi64)) - 4 * g;
+            }
         }
         // k-step kq of the products takes queries 16kq .. 16kq+15: registers
         // 8kq .. 8kq+7 (k-slot (g, e) is query 8*(e/4) + 4g + e%4 of the step),
@@ -559,21 +579,31 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
             for (int r4 = 2 * kq; r4 < 2 * kq + 2; ++r4) {
                 const f32x4 lv = *(const f32x4 *)(lt + 8 * r4 + 4 * g);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * r4 + e;
-                    float p = fast_exp2(fmaf(sa[r], c, -lv[e]));
-                    if (MASKED && (8 * r4 + e < lo || 8 * r4 + e > hi)) p = 0.f;
-                    sa[r] = p;
-                    pa[r] = p * pa[r];
-                }
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * r4 + e;
+                        float p = fast_exp2(fmaf(sa[kb][r], c, -lv[e]));
+                        if (MASKED && (8 * r4 + e < lo[kb] || 8 * r4 + e > hi[kb])) p = 0.f;
+                        sa[kb][r] = p;
+                        pa[kb][r] = p * pa[kb][r];
+                    }
             }
-            const bf16x8 pb = pack8(sa, 8 * kq), sb = pack8(pa, 8 * kq);
+            bf16x8 pb[KB], sb[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                pb[kb] = pack8(sa[kb], 8 * kq);
+                sb[kb] = pack8(pa[kb], 8 * kq);
+            }
 #pragma unroll
             for (int b = 0; b < D / 32; ++b) {
                 const bf16x8 ao = tr_pair<ROWB>(ot + kq * 16 * ROWB, toff[b]);
                 const bf16x8 aq = tr_pair<ROWB>(qt + kq * 16 * ROWB, toff[b]);
-                dvacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb, dvacc[b], 0, 0, 0);
-                dkacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb, dkacc[b], 0, 0, 0);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    dvacc[kb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[kb], dvacc[kb][b], 0, 0, 0);
+                    dkacc[kb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb[kb], dkacc[kb][b], 0, 0, 0);
+                }
             }
         }
     };
@@ -587,12 +617,12 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
     if (CAUSAL) {
         const int64_t a = kw0 - qoff - (BR - 1);  // first query tile whose last query sees kw0
         if (a > 0 && (a + BR - 1) / BR > its) its = (int)((a + BR - 1) / BR);
-        const int64_t f = kw0 + 31 - qoff;        // first tile whose first query sees every key
+        const int64_t f = kw0 + 32 * KB - 1 - qoff;  // first tile whose first query sees every key
         ifull = f > 0 ? (int)((f + BR - 1) / BR) : 0;
         if (ifull < its) ifull = its;
     }
     if (kw0 >= Nk) its = ifull = nqt;     // no keys: ring steps only
-    if (kw0 + 32 > Nk) ifull = nqt;        // ragged keys: every tile is masked
+    if (kw0 + 32 * KB > Nk) ifull = nqt;   // ragged keys: every tile is masked
     const int pend = (int)(Nq / BR);       // tiles before pend have no ragged queries
 
     auto ring = [&](int idx) __attribute__((always_inline)) {
@@ -614,7 +644,7 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
 #if FA_STATS
     uint32_t st_tiles = 0;
 #endif
-    f32x16 s0, p0, s1, p1;
+    Set s0, p0, s1, p1;
 #pragma unroll
     for (int t = 0; t <= GR; ++t)
         if (it0 + t < nqt) {
@@ -672,8 +702,12 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
     static_assert(ST * T::STAGEB >= W * 8192, "the ring holds the output stages");
     wait_vm<0>();
     lds_barrier();
-    store_rows_staged<D>(smem + wave_u * 8192, dkacc, scale, dK + bh * Nk * D, kw0, Nk, lane);
-    store_rows_staged<D>(smem + wave_u * 8192 + 4096, dvacc, 1.f, dV + bh * Nk * D, kw0, Nk, lane);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        store_rows_staged<D>(smem + wave_u * 8192, dkacc[kb], scale, dK + bh * Nk * D, kw0 + 32 * kb, Nk, lane);
+        store_rows_staged<D>(smem + wave_u * 8192 + 4096, dvacc[kb], 1.f, dV + bh * Nk * D, kw0 + 32 * kb,
+                             Nk, lane);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1006,6 +1040,13 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 #ifndef FA_BWD_DKDV_PIPE128
 #define FA_BWD_DKDV_PIPE128 1
 #endif
+// d = 64: waves per workgroup and 32-key blocks per wave of the pipelined
+// pass (8 and 1: two waves per SIMD; 4 and 2: one wave per SIMD whose Q and
+// dO fragments each serve two key blocks)
+#ifndef FA_BWD_PIPE_W64
+#define FA_BWD_PIPE_W64 8
+#define FA_BWD_PIPE_KB64 1
+#endif
 #ifndef FA_BWD_GR_PIPE128
 #define FA_BWD_GR_PIPE128 4
 #endif
@@ -1053,10 +1094,11 @@ hipError_t launch_main(const BwdArgs &a, hipStream_t s) {
     if constexpr (D == 64 ? FA_BWD_DKDV_PIPE : FA_BWD_DKDV_PIPE128) {
         // d = 128: four waves (one per SIMD: K, V, both accumulators and two
         // score sets take more than 256 registers)
-        constexpr int PW = D == 64 ? 8 : 4, PG = D == 64 ? FA_BWD_GR_PIPE : FA_BWD_GR_PIPE128;
-        using P = DkdvPipeCfg<D, PG, PW>;
+        constexpr int PW = D == 64 ? FA_BWD_PIPE_W64 : 4, PG = D == 64 ? FA_BWD_GR_PIPE : FA_BWD_GR_PIPE128;
+        constexpr int PK = D == 64 ? FA_BWD_PIPE_KB64 : 1;
+        using P = DkdvPipeCfg<D, PG, PW, PK>;
         const int nkt = (int)((a.Nk + P::KEYS - 1) / P::KEYS);
-        hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<D, PG, PW, CAUSAL>),
+        hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<D, PG, PW, PK, CAUSAL>),
                            dim3((unsigned)(a.B * a.H * nkt)), dim3(PW * 64), 0, s,
                            (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
                            (const uint16_t *)a.dO, a.L2, a.D, (uint16_t *)a.dK, (uint16_t *)a.dV,
