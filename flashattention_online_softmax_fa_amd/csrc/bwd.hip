@@ -622,6 +622,9 @@ void bwd_dkdv_pipe_kernel(const uint16_t *__restrict__ Q, const uint16_t *__rest
         if (ifull < its) ifull = its;
     }
     if (kw0 >= Nk) its = ifull = nqt;     // no keys: ring steps only
+    // keys after the last query's (causal): no query sees them, and the walk
+    // above would still take the ragged last tile, whose rows past Nq it counts
+    if (CAUSAL && kw0 > Nq - 1 + qoff) its = ifull = nqt;
     if (kw0 + 32 * KB > Nk) ifull = nqt;   // ragged keys: every tile is masked
     const int pend = (int)(Nq / BR);       // tiles before pend have no ragged queries
 
