@@ -1020,11 +1020,14 @@ void bwd_dq_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 #endif
 // d = 128, dQ pass: eight waves (one or two barriers per tile, 32- or 64-key
 // tiles) measured 4-5 % slower per backward than four waves with 32-key
-// tiles at 16 heads x 4096 and 2 x 16 heads x 2048 causal; 64-key tiles on
-// four waves were equal.
+// tiles at 16 heads x 4096 and 2 x 16 heads x 2048 causal.  With the
+// pipelined dK/dV pass, 64-key tiles on four waves (two 32-key blocks per
+// tile, the vector work of one beside the products of the next) are 1 %
+// faster at 32 heads x 8192 causal and 16 x 4 heads x 2048, level at
+// 2 x 16 heads x 4096 causal.
 #ifndef FA_BWD_W_DQ128  // waves per workgroup and keys per tile of the dQ pass, d = 128
 #define FA_BWD_W_DQ128 4
-#define FA_BWD_DQ_BC128 32
+#define FA_BWD_DQ_BC128 64
 #endif
 #ifndef FA_BWD_GR_DKDV128  // tiles per LDS barrier, d = 128 (one workgroup of four waves per CU)
 #define FA_BWD_GR_DKDV128 1
@@ -1136,7 +1139,7 @@ void bwd_bf16_tiles(int64_t d, int causal, int64_t *kv_rows, int64_t *kv_cols, i
     *kv_cols = d == 64 ? (causal ? DkdvChoice<64, true>::BR : DkdvChoice<64, false>::BR) : 32;
     if (d == 64 && FA_BWD_DKDV_PIPE) *kv_rows = *kv_cols = 32;
     *q_rows = d == 64 ? 32 * FA_BWD_DQ_QB64 : 32;
-    *q_cols = d == 64 ? FA_BWD_DQ_BC64 : 32;
+    *q_cols = d == 64 ? FA_BWD_DQ_BC64 : FA_BWD_DQ_BC128;
 }
 #endif
 
