@@ -1137,8 +1137,11 @@ void bwd_bf16_tiles(int64_t d, int causal, int64_t *kv_rows, int64_t *kv_cols, i
                     int64_t *q_cols) {
     *kv_rows = d == 64 ? (causal ? 32 * DkdvChoice<64, true>::KB : 32 * DkdvChoice<64, false>::KB) : 32;
     *kv_cols = d == 64 ? (causal ? DkdvChoice<64, true>::BR : DkdvChoice<64, false>::BR) : 32;
-    if (d == 64 && FA_BWD_DKDV_PIPE) *kv_rows = *kv_cols = 32;
-    *q_rows = d == 64 ? 32 * FA_BWD_DQ_QB64 : 32;
+    if (d == 64 && FA_BWD_DKDV_PIPE) {
+        *kv_rows = 32 * FA_BWD_PIPE_KB64;
+        *kv_cols = 32;
+    }
+    *q_rows = 32 * (d == 64 ? FA_BWD_DQ_QB64 : FA_BWD_DQ_QB128);
     *q_cols = d == 64 ? FA_BWD_DQ_BC64 : FA_BWD_DQ_BC128;
 }
 #endif
